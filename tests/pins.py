@@ -1,0 +1,314 @@
+"""Oracle pins: each function raises AssertionError when the oracle disagrees with
+something other than itself (closed forms, library routines, invariants the pages fix,
+brute force on tiny inputs). Used by test_oracle_*.py and, with mistakes planted in the
+oracle, by test_oracle_mutations.py."""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+import oracle.masked_attention
+import oracle.mask
+import oracle.norm
+import oracle.pipeline
+import oracle.rope
+import workloads as W
+from oracle.brute import brute_force
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+C, F, G = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA
+
+
+def small_workload(segs, hq=4, hkv=2, d=16, rope="mrope", sections=(4, 2, 2), norm=True,
+                   batch=1, seed=7, theta=1e4, dtype="f32"):
+    return W.Workload(name="small", description="small", batch=batch, segments=tuple(segs),
+                      n_q_heads=hq, n_kv_heads=hkv, head_dim=d, dtype=dtype, rope=rope,
+                      rope_theta=theta, mrope_sections=sections, qk_norm=norm, norm_eps=1e-6,
+                      seed=seed)
+
+
+def closed_form_pairs(segments, S):
+    """Allowed pairs from arithmetic series, one term per segment: a causal segment
+    [a, a+L) contributes sum_{i=a}^{a+L-1} (i+1); a full one L*S; an image (GCA)
+    segment L*(a+L), since each of its rows sees every key before the segment end."""
+    total = 0
+    for a, L, kind in segments:
+        a, L = int(a), int(L)
+        if kind == C:
+            total += L * a + L * (L + 1) // 2
+        elif kind == F:
+            total += L * S
+        else:
+            total += L * (a + L)
+    return total
+
+
+# ---------------------------------------------------------------- mask
+def pin_pair_counts():
+    gold = json.load(open(os.path.join(GOLDEN, "pair_counts.json")))["counts"]
+    for name, w in W.CONFIGS.items():
+        table = W.segment_table(w)[0]
+        got = oracle.mask.explicit_mask(table, w.seq_len).sum()
+        assert got == closed_form_pairs(table, w.seq_len), name
+        assert got == gold[name]["allowed_pairs_per_batch_item"], name
+
+
+def pin_mask_elementwise_bruteforce():
+    from oracle.brute import _allowed
+    layouts = [[(C, 5), (F, 7), (C, 4)], [(C, 3), (G, 6), (C, 2), (G, 5), (G, 3), (C, 1)],
+               [(G, 9)], [(F, 4), (C, 6)]]
+    for segs in layouts:
+        w = small_workload([W.Segment(k, n) for k, n in segs])
+        table = W.segment_table(w)[0]
+        M = oracle.mask.explicit_mask(table, w.seq_len)
+        for i in range(w.seq_len):
+            for j in range(w.seq_len):
+                assert M[i, j] == _allowed(table, i, j), (segs, i, j)
+
+
+def pin_mask_special_cases():
+    S = 37
+    tril = np.tril(np.ones((S, S), dtype=bool))
+    t = np.array([[0, S, C]])
+    assert np.array_equal(oracle.mask.explicit_mask(t, S), tril)
+    for kind in (F, G):
+        assert oracle.mask.explicit_mask(np.array([[0, S, kind]]), S).all()
+    # the first text row attends only to itself
+    t = np.array([[0, 10, C], [10, 27, F]])
+    M = oracle.mask.explicit_mask(t, S)
+    assert M[0, 0] and not M[0, 1:].any()
+    # every row is a key prefix [0, lim), with lim > i (no empty row)
+    t = np.array([[0, 5, C], [5, 9, G], [14, 3, C], [17, 12, G], [29, 8, F]])
+    M = oracle.mask.explicit_mask(t, S)
+    for i in range(S):
+        lim = M[i].sum()
+        assert lim > i and M[i, :lim].all() and not M[i, lim:].any()
+    # merging adjacent causal or full segments changes nothing; splitting an image does
+    a = oracle.mask.explicit_mask(np.array([[0, 10, C], [10, 27, C]]), S)
+    assert np.array_equal(a, tril)
+    b = oracle.mask.explicit_mask(np.array([[0, 20, G], [20, 17, G]]), S)
+    assert not np.array_equal(b, oracle.mask.explicit_mask(np.array([[0, S, G]]), S))
+
+
+# ---------------------------------------------------------------- RMSNorm
+def pin_rmsnorm_library():
+    rng = np.random.default_rng(3)
+    for scale in (1.0, 1e-3):   # small inputs make eps matter
+        x = rng.standard_normal((5, 7, 3, 64)) * scale
+        w = 1 + 0.02 * rng.standard_normal(64)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(w),
+                                           eps=1e-6).numpy()
+        got = oracle.norm.rms_norm(x, w, 1e-6)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-15), scale
+
+
+def pin_rmsnorm_closed_form():
+    # d = 4, x = (3, 4, 0, 0): mean square 25/4, so with eps 0, y = x / 2.5 * w
+    y = oracle.norm.rms_norm(np.array([3.0, 4.0, 0.0, 0.0]), np.array([1.0, 2.0, 3.0, 4.0]), 0.0)
+    assert np.allclose(y, [1.2, 3.2, 0.0, 0.0], rtol=0, atol=1e-15)
+    # with unit weights the output mean square is ms / (ms + eps)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((100, 32)) * 0.01
+    eps = 1e-4
+    y = oracle.norm.rms_norm(x, np.ones(32), eps)
+    ms = np.mean(x * x, axis=-1)
+    assert np.allclose(np.mean(y * y, axis=-1), ms / (ms + eps), rtol=1e-12)
+    assert np.array_equal(oracle.norm.rms_norm(np.zeros(8), np.ones(8), 1e-6), np.zeros(8))
+
+
+# ---------------------------------------------------------------- rotary
+def _rot(x, pos, kind, sections=(0, 0, 0), base=1e4):
+    d = x.shape[-1]
+    axes = oracle.rope.axis_of_pair(kind, d, sections)
+    ang = oracle.rope.rope_angles(pos, axes, oracle.rope.inv_freq(base, d))
+    return oracle.rope.apply_rope(x, ang)
+
+
+def pin_rope_reduces_to_1d():
+    """2D (and 3-axis) rotary with every axis equal to n is 1D rotary at n, bit for bit
+    (HunyuanImage 3.0 digest: with no image tokens the encoding reduces exactly to 1D)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 50, 3, 128))
+    n = rng.integers(0, 9000, size=(2, 50))
+    one = _rot(x, n[..., None], "1d")
+    assert np.array_equal(_rot(x, np.repeat(n[..., None], 2, -1), "2d"), one)
+    assert np.array_equal(_rot(x, np.repeat(n[..., None], 3, -1), "mrope", (24, 20, 20), 5e6),
+                          _rot(x, n[..., None], "1d", base=5e6))
+
+
+def pin_rope_relative_position():
+    """Scores depend on the position difference only (HunyuanImage 3.0 digest, 1D RoPE
+    property), per axis for the multi-axis forms."""
+    rng = np.random.default_rng(6)
+    for kind, A, sec in (("1d", 1, (0, 0, 0)), ("2d", 2, (0, 0, 0)), ("mrope", 3, (24, 20, 20))):
+        q = rng.standard_normal((1, 20, 1, 128))
+        k = rng.standard_normal((1, 20, 1, 128))
+        p = rng.integers(0, 3000, size=(1, 20, A))
+        s0 = np.einsum("bihd,bjhd->ij", _rot(q, p, kind, sec), _rot(k, p, kind, sec))
+        for a in range(A):
+            shift = np.zeros(A, dtype=np.int64)
+            shift[a] = 1234
+            s1 = np.einsum("bihd,bjhd->ij", _rot(q, p + shift, kind, sec),
+                           _rot(k, p + shift, kind, sec))
+            assert np.abs(s1 - s0).max() < 1e-9 * np.abs(s0).max(), (kind, a)
+
+
+def pin_rope_rotation_forms():
+    """Rotate-half rotary equals multiplying z_i = x_i + i*x_{i+d/2} by exp(i*angle_i);
+    it preserves the norm; position 0 is the identity."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((1, 30, 2, 64))
+    pos = rng.integers(0, 500, size=(1, 30, 2))
+    y = _rot(x, pos, "2d")
+    axes = np.arange(32) % 2
+    ang = pos[..., axes].astype(np.float64) * 1e4 ** (-np.arange(32) / 32.0)
+    z = (x[..., :32] + 1j * x[..., 32:]) * np.exp(1j * ang)[:, :, None, :]
+    assert np.allclose(y[..., :32], z.real, atol=1e-12) and np.allclose(y[..., 32:], z.imag,
+                                                                         atol=1e-12)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    assert np.array_equal(_rot(x, np.zeros_like(pos), "2d"), x)
+
+
+def pin_rope_tables():
+    gold = json.load(open(os.path.join(GOLDEN, "page_shapes.json")))
+    sec = tuple(gold["mrope_sections"])
+    axes = oracle.rope.axis_of_pair("mrope", gold["head_dim"], sec)
+    assert [int((axes == a).sum()) for a in range(3)] == list(sec)
+    # interleaved: the first 60 pairs cycle T, H, W; the rest are T
+    assert list(axes[:6]) == [0, 1, 2, 0, 1, 2] and (axes[60:] == 0).all()
+    assert list(oracle.rope.axis_of_pair("2d", 8)) == [0, 1, 0, 1]
+    f = oracle.rope.inv_freq(5e6, 128)
+    assert f[0] == 1.0 and np.allclose(f[1:] / f[:-1], 5e6 ** (-2 / 128), rtol=1e-13)
+    assert len(f) == 64
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch CPU fp64 scaled_dot_product_attention on [S][H][d] inputs (K/V per q head)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(np.transpose(a, (1, 0, 2))))
+    am = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=am,
+                                                         is_causal=causal)
+    return np.transpose(o.numpy(), (1, 0, 2))
+
+
+def pin_attention_library():
+    rng = np.random.default_rng(9)
+    S, H, d = 61, 3, 32
+    q, k, v = (rng.standard_normal((1, S, H, d)) for _ in range(3))
+    # pure text: causal attention (BASELINE property; digest: text tokens are causal)
+    M = oracle.mask.explicit_mask(np.array([[0, S, C]]), S)
+    got = oracle.masked_attention.attention(q, k, v, [M])
+    assert np.allclose(got[0], _sdpa(q[0], k[0], v[0], causal=True), atol=1e-12)
+    # all-full: unmasked attention
+    M = oracle.mask.explicit_mask(np.array([[0, S, F]]), S)
+    got = oracle.masked_attention.attention(q, k, v, [M])
+    assert np.allclose(got[0], _sdpa(q[0], k[0], v[0]), atol=1e-12)
+    # hybrid mask passed to the library as a boolean mask
+    M = oracle.mask.explicit_mask(np.array([[0, 9, C], [9, 20, G], [29, 7, C], [36, 25, F]]), S)
+    got = oracle.masked_attention.attention(q, k, v, [M], row_chunk=16)
+    assert np.allclose(got[0], _sdpa(q[0], k[0], v[0], mask=M), atol=1e-12)
+
+
+def pin_attention_gqa():
+    """GQA with 4 query heads per KV head equals MHA on K/V repeated per query head."""
+    rng = np.random.default_rng(10)
+    S = 33
+    q = rng.standard_normal((1, S, 8, 16))
+    k = rng.standard_normal((1, S, 2, 16))
+    v = rng.standard_normal((1, S, 2, 16))
+    M = oracle.mask.explicit_mask(np.array([[0, 11, C], [11, 22, F]]), S)
+    gqa = oracle.masked_attention.attention(q, k, v, [M])
+    for h in range(8):
+        ref = _sdpa(q[0, :, h:h + 1], k[0, :, h // 4:h // 4 + 1], v[0, :, h // 4:h // 4 + 1],
+                    mask=M)
+        assert np.allclose(gqa[0, :, h:h + 1], ref, atol=1e-12), h
+
+
+def pin_attention_invariants():
+    rng = np.random.default_rng(11)
+    w = small_workload([W.Segment(C, 6), W.Segment(G, 9), W.Segment(C, 4), W.Segment(F, 5)],
+                       rope="2d", sections=(0, 0, 0))
+    x = W.generate(w)
+    out = oracle.pipeline.hot_path(x)
+    # row 0 sees only itself: its output is v_0 of its KV head
+    assert np.array_equal(out[0, 0], x.v[0, 0][np.arange(4) // 2])
+    # a causal row does not depend on later tokens; an image row depends on its own
+    # segment's later tokens but not on tokens past the segment end
+    def perturb(i0, i1):
+        y = W.generate(w)
+        y.q[0, i0:i1] += 1.0
+        y.k[0, i0:i1] += 1.0
+        y.v[0, i0:i1] += 1.0
+        return oracle.pipeline.hot_path(y)
+    o2 = perturb(16, 24)                      # tokens 16.. : after text row 5, after image
+    assert np.array_equal(o2[0, :15], out[0, :15])
+    o3 = perturb(14, 15)                      # last token of the image segment [6, 15)
+    assert not np.allclose(o3[0, 6], out[0, 6])
+    assert np.array_equal(o3[0, :6], out[0, :6])
+    # uniform probe: q = 0 gives uniform weights over the allowed prefix, so with one-hot
+    # values the output is the fraction of allowed keys per value channel
+    y = W.generate(w)
+    y.q[:] = 0.0
+    y.v[:] = 0.0
+    S, d = w.seq_len, w.head_dim
+    for j in range(S):
+        y.v[0, j, :, j % d] = 1.0
+    o4 = oracle.pipeline.hot_path(y)
+    lims = {0: lambda i: i + 1}
+    for i in range(S):
+        lim = int(oracle.mask.mask_rows(y.segments[0], S, [i])[0].sum())
+        expect = np.zeros(d)
+        for j in range(lim):
+            expect[j % d] += 1.0 / lim
+        assert np.allclose(o4[0, i, 0], expect, atol=1e-14), i
+
+
+def pin_bruteforce():
+    cases = [W.get_config("tiny"),
+             small_workload([W.Segment(C, 7), W.Segment(F, 9, (3, 3)), W.Segment(C, 4, (2, 2))],
+                            rope="mrope", sections=(4, 2, 2), norm=True, batch=2),
+             small_workload([W.Segment(C, 5), W.Segment(G, 6, (2, 3)), W.Segment(C, 3),
+                             W.Segment(G, 4, (2, 2)), W.Segment(C, 2)], rope="2d", norm=False,
+                            hq=2, hkv=1, d=8)]
+    for w in cases:
+        x = W.generate(w)
+        assert np.abs(np.array(brute_force(x)) - oracle.pipeline.hot_path(x)).max() < 1e-12, w.name
+
+
+# ---------------------------------------------------------------- tiles
+def closed_form_labels(segments, S, bq, bk):
+    """Labels from per-row key limits: a causal row i sees [0, i+1), a full row [0, S),
+    an image row [0, end of its segment). Every row is a prefix, so per query block
+    tiles below floor(min lim / bk) are FULL (all of them if min lim = S), tiles from
+    ceil(max lim / bk) on are SKIP, and the rest PARTIAL."""
+    lim = np.empty(S, dtype=np.int64)
+    for a, L, kind in segments:
+        i = np.arange(a, a + L)
+        lim[a:a + L] = i + 1 if kind == C else (S if kind == F else a + L)
+    nq, nk = -(-S // bq), -(-S // bk)
+    out = np.empty((nq, nk), dtype=np.uint8)
+    for qb in range(nq):
+        l = lim[qb * bq:(qb + 1) * bq]
+        kfull = nk if l.min() >= S else l.min() // bk
+        kend = -(-l.max() // bk)
+        out[qb] = [1 if kb < kfull else (2 if kb < kend else 0) for kb in range(nk)]
+    return out
+
+
+def pin_tile_labels():
+    gold = json.load(open(os.path.join(GOLDEN, "tile_counts.json")))["counts"]
+    for name, w in W.CONFIGS.items():
+        table = W.segment_table(w)[0]
+        M = oracle.mask.explicit_mask(table, w.seq_len)
+        for bq, bk in ((64, 64), (128, 64), (32, 64)):
+            lab = oracle.tile_labels(M, bq, bk)
+            assert np.array_equal(lab, closed_form_labels(table, w.seq_len, bq, bk)), (name, bq)
+        lab = oracle.tile_labels(M, 64, 64)
+        assert [int((lab == t).sum()) for t in (0, 1, 2)] == [
+            gold[name]["skip"], gold[name]["full"], gold[name]["partial"]], name

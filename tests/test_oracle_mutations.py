@@ -1,0 +1,167 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that a pin catches each.
+
+Each case replaces one oracle function with a wrong variant (a dropped term, a wrong
+sign, index or operand) and asserts that at least one of the listed pins fails."""
+import numpy as np
+import pytest
+
+import oracle.mask
+import oracle.masked_attention
+import oracle.norm
+import oracle.pipeline
+import oracle.rope
+import pins
+
+
+def _rope_sign(x, angles, dtype=np.float64):
+    x = np.asarray(x, dtype=dtype)
+    h = x.shape[-1] // 2
+    c = np.cos(angles)[:, :, None, :]
+    s = np.sin(angles)[:, :, None, :]
+    return np.concatenate([x[..., :h] * c + x[..., h:] * s, x[..., h:] * c - x[..., :h] * s], -1)
+
+
+def _rope_adjacent_pairs(x, angles, dtype=np.float64):
+    x = np.asarray(x, dtype=dtype)
+    c = np.cos(angles)[:, :, None, :]
+    s = np.sin(angles)[:, :, None, :]
+    y = np.empty_like(x)
+    y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    y[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * s
+    return y
+
+
+def _inv_freq_half(base, d):
+    return np.float64(base) ** (-np.arange(d // 2) / d)
+
+
+def _axes_contiguous(kind, d, sections=(0, 0, 0)):
+    if kind == "mrope":
+        return np.repeat(np.arange(3), sections)
+    return pins_axis(kind, d, sections)
+
+
+pins_axis = oracle.rope.axis_of_pair
+
+
+def _norm_eps_outside(x, w, eps, dtype=np.float64):
+    x = np.asarray(x, dtype=dtype)
+    return x / (np.sqrt(np.mean(x * x, -1, keepdims=True)) + eps) * w
+
+
+def _norm_no_weight(x, w, eps, dtype=np.float64):
+    x = np.asarray(x, dtype=dtype)
+    return x / np.sqrt(np.mean(x * x, -1, keepdims=True) + eps)
+
+
+def _norm_sum_not_mean(x, w, eps, dtype=np.float64):
+    x = np.asarray(x, dtype=dtype)
+    return x / np.sqrt(np.sum(x * x, -1, keepdims=True) + eps) * w
+
+
+def _mask_strict_causal(segments, S, rows):
+    M = _orig_mask_rows(segments, S, rows)
+    table = np.asarray(segments)
+    seg = oracle.mask.segment_ids(segments, S)
+    for r, i in enumerate(np.asarray(rows)):
+        if table[seg[i], 2] == 0 and i > 0:
+            M[r, i] = False
+    return M
+
+
+def _mask_gca_no_segment(segments, S, rows):
+    M = _orig_mask_rows(segments, S, rows)
+    table = np.asarray(segments)
+    seg = oracle.mask.segment_ids(segments, S)
+    j = np.arange(S)
+    for r, i in enumerate(np.asarray(rows)):
+        if table[seg[i], 2] == 2:
+            M[r] = j <= i
+    return M
+
+
+_orig_mask_rows = oracle.mask.mask_rows
+_orig_attention = oracle.masked_attention.attention
+
+
+def _attn_no_scale(q, k, v, masks, scale=None, **kw):
+    return _orig_attention(q, k, v, masks, scale=1.0, **kw)
+
+
+def _attn_k_for_v(q, k, v, masks, scale=None, **kw):
+    return _orig_attention(q, k, k, masks, scale=scale, **kw)
+
+
+def _attn_gqa_modulo(q, k, v, masks, scale=None, dtype=np.float64, heads=None, row_chunk=1024):
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    out = np.empty((B, S, Hq, d))
+    for h in range(Hq):
+        g = h % Hkv
+        out[:, :, h:h + 1] = _orig_attention(q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1],
+                                             masks, scale=(1 / np.sqrt(d)) if scale is None else scale)
+    return out
+
+
+def _attn_transposed_scores(q, k, v, masks, scale=None, dtype=np.float64, heads=None,
+                            row_chunk=1024):
+    B, S, Hq, d = q.shape
+    group = Hq // k.shape[2]
+    scale = 1 / np.sqrt(d) if scale is None else scale
+    out = np.empty((B, S, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            Q, K, V = q[b, :, h], k[b, :, h // group], v[b, :, h // group]
+            Z = np.where(masks[b], (K @ Q.T) * scale, -np.inf)
+            Z = np.exp(Z - Z.max(-1, keepdims=True))
+            out[b, :, h] = (Z / Z.sum(-1, keepdims=True)) @ V
+    return out
+
+
+MUTATIONS = {
+    "rope_sign": ([(oracle.rope, "apply_rope", _rope_sign), (oracle.pipeline, "apply_rope", _rope_sign)],
+                  ["pin_rope_rotation_forms"]),
+    "rope_adjacent_pairs": ([(oracle.rope, "apply_rope", _rope_adjacent_pairs),
+                             (oracle.pipeline, "apply_rope", _rope_adjacent_pairs)],
+                            ["pin_rope_rotation_forms", "pin_bruteforce"]),
+    "rope_freq_exponent": ([(oracle.rope, "inv_freq", _inv_freq_half),
+                            (oracle.pipeline, "inv_freq", _inv_freq_half)],
+                           ["pin_rope_tables", "pin_bruteforce"]),
+    "mrope_contiguous_sections": ([(oracle.rope, "axis_of_pair", _axes_contiguous),
+                                   (oracle.pipeline, "axis_of_pair", _axes_contiguous)],
+                                  ["pin_rope_tables", "pin_bruteforce"]),
+    "norm_eps_outside_sqrt": ([(oracle.norm, "rms_norm", _norm_eps_outside)],
+                              ["pin_rmsnorm_library"]),
+    "norm_no_weight": ([(oracle.norm, "rms_norm", _norm_no_weight),
+                        (oracle.pipeline, "rms_norm", _norm_no_weight)],
+                       ["pin_rmsnorm_library", "pin_rmsnorm_closed_form", "pin_bruteforce"]),
+    "norm_sum_not_mean": ([(oracle.norm, "rms_norm", _norm_sum_not_mean)],
+                          ["pin_rmsnorm_library", "pin_rmsnorm_closed_form"]),
+    "mask_strict_causal": ([(oracle.mask, "mask_rows", _mask_strict_causal)],
+                           ["pin_pair_counts", "pin_mask_special_cases",
+                            "pin_mask_elementwise_bruteforce"]),
+    "mask_gca_without_segment": ([(oracle.mask, "mask_rows", _mask_gca_no_segment)],
+                                 ["pin_pair_counts", "pin_mask_special_cases"]),
+    "attn_dropped_scale": ([(oracle.masked_attention, "attention", _attn_no_scale)],
+                           ["pin_attention_library"]),
+    "attn_k_used_as_v": ([(oracle.masked_attention, "attention", _attn_k_for_v)],
+                         ["pin_attention_library"]),
+    "attn_gqa_modulo_map": ([(oracle.masked_attention, "attention", _attn_gqa_modulo)],
+                            ["pin_attention_gqa"]),
+    "attn_transposed_scores": ([(oracle.masked_attention, "attention", _attn_transposed_scores)],
+                               ["pin_attention_library"]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    patches, pin_names = MUTATIONS[name]
+    for mod, attr, fn in patches:
+        monkeypatch.setattr(mod, attr, fn)
+    caught = []
+    for p in pin_names:
+        try:
+            getattr(pins, p)()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(p)
+    assert caught, f"mutation {name} passed every pin in {pin_names}"
