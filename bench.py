@@ -1,0 +1,209 @@
+"""Benchmark of the hybrid-mask attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input resident in HBM:
+  ha_classify_tiles  (segment table -> row limits + tile ranges)
+  ha_qk_prologue     (q/k RMSNorm + 3-axis interleaved mRoPE)
+  ha_attn_fwd_planned (hybrid-mask GQA flash attention)
+on the HiDream-O1-style 2048^2 text-to-image workload: batch 2 (CFG cond/uncond), 258
+causal tokens (256 text + 2 markers) then 4096 generation patches (64x64 grid) with full
+attention; GQA 32/8, head dim 128, bf16.
+
+Metric: useful (mask-aware) attention TFLOP/s, 4 * d * Hq * (allowed query-key pairs) per
+pass, over the whole step. HIP events on the launch stream bracket each kernel of every
+timed step, which gives the attention kernel's own duration for the MFMA roofline, and
+the prologue's for its HBM roofline. Three copies of the inputs are cycled so the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+    python bench.py [--steps K] [--warmup W] [--workload hd2048] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+BF16_PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz
+HBM_PEAK_GBPS = 8000.0
+METRIC = "hybrid-mask attention TFLOP/s (useful) and % bf16 MFMA peak, 1 MI355X"
+ATTN_SRC = os.path.join(ROOT, "unified_text_pixel_amd", "csrc", "ha_attn_fwd.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "attn_hd2048_counters.json")
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def attn_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs, or None
+    when the kernel source has changed since they were taken."""
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def allowed_pairs(segments: np.ndarray, S: int) -> int:
+    """Allowed query-key pairs of one batch item, summed per segment in closed form:
+    causal [a, a+L) -> sum (i+1); full -> L*S; image (generalized causal) -> L*(a+L)."""
+    n = 0
+    for a, L, kind in segments:
+        a, L = int(a), int(L)
+        n += L * a + L * (L + 1) // 2 if kind == 0 else (L * S if kind == 1 else L * (a + L))
+    return n
+
+
+def cpu_baseline(w, x, target_s=12.0):
+    """Time the oracle, as it is, on a bounded sample of the same workload: batch item 0 and
+    the query heads of as many KV groups as fit about target_s seconds (at least one)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    import workloads as W
+
+    sub = W.Inputs(workload=w.replace(batch=1), q=x.q[:1], k=x.k[:1], v=x.v[:1], q_bits=None,
+                   k_bits=None, v_bits=None, w_q=x.w_q, w_k=x.w_k, positions=x.positions[:1],
+                   segments=x.segments[:1])
+    group = w.n_q_heads // w.n_kv_heads
+    pairs = allowed_pairs(x.segments[0], w.seq_len)
+    heads, elapsed = 0, 0.0
+    while heads < w.n_q_heads and (heads == 0 or elapsed * (heads + group) / heads < target_s):
+        t0 = time.perf_counter()
+        oracle.hot_path(sub, heads=range(heads, heads + group))
+        elapsed += time.perf_counter() - t0
+        heads += group
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    flops = 4.0 * w.head_dim * heads * pairs
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"batch item 0, query heads 0-{heads - 1} ({heads} of {w.n_q_heads}), whole "
+                      f"path (norm, mRoPE, explicit mask, fp64 attention), {elapsed:.1f} s; "
+                      f"host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="hd2048")
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from unified_text_pixel_amd import api, binding as B
+    from workloads.device import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load_library()
+    w = W.get_config(args.workload)
+    print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = W.generate(w)
+    dev = to_device(x)
+    desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype,
+                      x.segments)
+    cs = api.rope_table(w.rope_theta, w.head_dim, w.seq_len) if w.rope != "none" else None
+    pro = B.PrologueDesc(w.rope, dev["positions"], cs, 0 if cs is None else cs.shape[0],
+                         dev["w_q"], dev["w_k"], w.norm_eps, w.mrope_sections)
+    bq, bk, nq, nk = B.ha_tile_shape(desc)
+    sets = []
+    for _ in range(args.sets):
+        sets.append({
+            "q": dev["q"].clone(), "k": dev["k"].clone(), "v": dev["v"].clone(),
+            "qr": torch.empty_like(dev["q"]), "kr": torch.empty_like(dev["k"]),
+            "out": torch.empty_like(dev["q"]),
+            "ranges": torch.empty((w.batch, nq, 2), dtype=torch.int32, device="cuda"),
+            "lim": torch.empty((w.batch, w.seq_len), dtype=torch.int32, device="cuda"),
+        })
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        if ev:
+            ev[0].record(stream)
+        B.ha_classify_tiles(desc, None, s["ranges"], s["lim"], stream)
+        if ev:
+            ev[1].record(stream)
+        B.ha_qk_prologue(desc, pro, s["q"], s["k"], s["qr"], s["kr"], stream)
+        if ev:
+            ev[2].record(stream)
+        B.ha_attn_fwd_planned(desc, s["qr"], s["kr"], s["v"], s["lim"], s["ranges"], s["out"],
+                              stream)
+        if ev:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+    cls_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    pro_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    att_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    pairs = sum(allowed_pairs(x.segments[b], w.seq_len) for b in range(w.batch))
+    useful = 4.0 * w.head_dim * w.n_q_heads * pairs
+    att_s = float(att_ms.mean()) / 1e3
+    att_tflops = useful / att_s / 1e12
+    elem = 2 if w.dtype == "bf16" else 4
+    pro_bytes = 2.0 * elem * w.batch * w.seq_len * (w.n_q_heads + w.n_kv_heads) * w.head_dim
+    pro_gbps = pro_bytes / (float(pro_ms.mean()) / 1e3) / 1e9
+    traffic = attn_traffic()
+
+    rec = {
+        "metric": METRIC,
+        "value": useful / (step_ms / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
+                   "seq_len": w.seq_len, "segments": x.segments[0].tolist(),
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "rope": w.rope, "qk_norm": w.qk_norm, "allowed_pairs": pairs,
+                   "useful_gflop_per_step": useful / 1e9, "tile": [bq, bk]},
+        "attn_kernel_ms": {"mean": float(att_ms.mean()), "median": float(np.median(att_ms)),
+                           "p10": float(np.percentile(att_ms, 10)),
+                           "p90": float(np.percentile(att_ms, 90))},
+        "attn_tflops": att_tflops,
+        "pct_bf16_peak": 100.0 * att_tflops / BF16_PEAK_TFLOPS,
+        "prologue_ms": float(pro_ms.mean()), "prologue_gbps": pro_gbps,
+        "classify_ms": float(cls_ms.mean()),
+        "roofline": {"bound": "mfma", "achieved": att_tflops, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": att_tflops / BF16_PEAK_TFLOPS,
+                     "traffic": traffic},
+        "prologue_roofline": {"bound": "hbm", "achieved": pro_gbps, "peak": HBM_PEAK_GBPS,
+                              "unit": "GB/s", "frac": pro_gbps / HBM_PEAK_GBPS},
+        "attn_kernel_sha": kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * ha_attn.h -- hybrid-masked joint self-attention for unified text+pixel image
+ * transformers, on AMD Instinct MI355X (gfx950).
+ *
+ * One sequence holds text, condition and generation tokens; each token carries a segment
+ * type that fixes which keys its query row may attend to:
+ *   HA_SEG_CAUSAL  text, markers, condition and reference tokens: keys j <= i
+ *                  (HiDream-O1 atlas page, "How it works"; hidream-o1-p100a model card,
+ *                  "What this model is"; HunyuanImage 3.0 digest, "Generalized Causal
+ *                  Attention", text rows)
+ *   HA_SEG_FULL    HiDream-O1 generation tokens: every key of the sequence (same pages)
+ *   HA_SEG_GCA     HunyuanImage 3.0 image tokens: keys j <= i plus every key of their own
+ *                  image segment (HunyuanImage 3.0 digest, "Generalized Causal Attention",
+ *                  the core rule)
+ * Scores use GQA (consecutive groups of n_q_heads / n_kv_heads query heads share one KV
+ * head), optional q/k RMSNorm and 1D / generalized 2D / 3-axis interleaved rotary
+ * embeddings (hidream-o1-p100a model card, architecture paragraph; HunyuanImage 3.0
+ * digest, "Generalized 2D Rotary Position Embedding").
+ *
+ * Conventions shared by every entry point
+ *  - Layouts: q and out are [batch][seq_len][n_q_heads][head_dim]; k and v are
+ *    [batch][seq_len][n_kv_heads][head_dim]; all contiguous, token-major, in the dtype of
+ *    the descriptor (bf16 or fp32). Device pointers must be 16-byte aligned.
+ *  - Ownership: the caller owns every buffer. The library allocates no device memory;
+ *    scratch space comes from the caller's workspace. Inputs are never written, except
+ *    through the explicit q_out == q_in / k_out == k_in alias of ha_qk_prologue.
+ *  - Streams: every launch is asynchronous on the caller's hipStream_t, passed as void*
+ *    (NULL = the default stream). No call synchronises, unless the environment variable
+ *    HA_DEBUG=1 is set, which synchronises and checks for errors after each launch.
+ *  - Errors: every argument is validated on the host before any HIP call. A bad call
+ *    returns a nonzero ha_status, sets the thread's ha_last_error() text, and touches
+ *    neither the device nor the stream. A failed launch returns HA_ERR_HIP with the HIP
+ *    error text. No C++ exception crosses this interface. The library keeps no state
+ *    between calls apart from that error text.
+ *  - Empty work (batch == 0 or seq_len == 0) is valid and launches nothing.
+ */
+#ifndef HA_ATTN_H
+#define HA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HA_ABI_VERSION 1
+#define HA_MAX_SEGMENTS 64      /* segments per batch item */
+#define HA_MAX_SEQ_LEN (1 << 22)
+
+typedef enum {
+  HA_OK = 0,
+  HA_ERR_INVALID_ARG = 1,   /* null pointer, bad count, bad enum, bad scale/eps */
+  HA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, head ratio, sizes) */
+  HA_ERR_SEGMENTS = 3,      /* segment table does not tile [0, seq_len) */
+  HA_ERR_ALIGNMENT = 4,     /* device pointer not 16-byte (weights: 4-byte) aligned */
+  HA_ERR_WORKSPACE = 5,     /* workspace missing, too small or not 256-byte aligned */
+  HA_ERR_HIP = 6            /* a HIP launch or runtime call failed */
+} ha_status;
+
+typedef enum { HA_SEG_CAUSAL = 0, HA_SEG_FULL = 1, HA_SEG_GCA = 2 } ha_seg_kind;
+typedef enum { HA_DTYPE_BF16 = 0, HA_DTYPE_F32 = 1 } ha_dtype;
+typedef enum { HA_ROPE_NONE = 0, HA_ROPE_1D = 1, HA_ROPE_2D = 2, HA_ROPE_MROPE = 3 } ha_rope_kind;
+typedef enum { HA_TILE_SKIP = 0, HA_TILE_FULL = 1, HA_TILE_PARTIAL = 2 } ha_tile_label;
+
+/* One segment of one batch item: tokens [start, start + length) of kind ha_seg_kind.
+ * A batch item's segments must be listed in order, contiguous from 0, with positive
+ * lengths summing to seq_len. Adjacent HA_SEG_GCA segments are distinct images. */
+typedef struct {
+  int32_t start;
+  int32_t length;
+  int32_t kind;
+} ha_segment;
+
+typedef struct {
+  int32_t batch;            /* >= 0 */
+  int32_t seq_len;          /* >= 0, <= HA_MAX_SEQ_LEN */
+  int32_t n_q_heads;        /* >= 1 */
+  int32_t n_kv_heads;       /* >= 1, divides n_q_heads; n_q_heads / n_kv_heads in {1,2,4,8} */
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t dtype;            /* ha_dtype of q, k, v, out */
+  const ha_segment* segments; /* HOST memory, [batch][n_segments] */
+  int32_t n_segments;       /* 1 .. HA_MAX_SEGMENTS (per batch item) */
+  float scale;              /* softmax scale; 0 means 1 / sqrt(head_dim) */
+} ha_attn_desc;
+
+/* q/k prologue: RMSNorm over head_dim (y = x / sqrt(mean(x^2) + eps) * w, before the
+ * rotation; model card "q/k RMSNorm"), then the rotary embedding. Pair i of a head is
+ * (x[i], x[i + head_dim/2]) and is rotated by angle positions[axis(i)] * theta^(-2i/d):
+ *   HA_ROPE_1D     axis(i) = 0                      (positions [B][S][1])
+ *   HA_ROPE_2D     axis(i) = i mod 2, 0 = x (column), 1 = y (row)   ([B][S][2])
+ *   HA_ROPE_MROPE  pairs dealt to axes 0,1,2 (T, H, W) in turn, each axis leaving the
+ *                  rotation once it holds mrope_sections[axis] pairs ([B][S][3]);
+ *                  [24,20,20] gives i mod 3 for i < 60 and T for 60..63
+ *   HA_ROPE_NONE   no rotation (positions and cos_sin may be NULL)
+ * Positions outside [0, n_pos) are clamped to that range. */
+typedef struct {
+  int32_t rope_kind;            /* ha_rope_kind */
+  int32_t mrope_sections[3];    /* HA_ROPE_MROPE only; non-negative, sum head_dim / 2 */
+  const int32_t* positions;     /* DEVICE [batch][seq_len][n_axes] */
+  const float* cos_sin;         /* DEVICE [n_pos][head_dim/2][2] from ha_rope_table_fill */
+  int32_t n_pos;                /* rows of cos_sin */
+  const float* q_norm_weight;   /* DEVICE fp32 [head_dim], or NULL for no RMSNorm */
+  const float* k_norm_weight;   /* DEVICE fp32 [head_dim]; NULL exactly when q's is */
+  float eps;                    /* RMSNorm epsilon, >= 0 */
+} ha_prologue_desc;
+
+/* HA_ABI_VERSION of the built library. */
+int ha_abi_version(void);
+
+/* Text of the calling thread's last error ("" if none). Never NULL. */
+const char* ha_last_error(void);
+
+/* Fill host_out [n_pos][head_dim/2][2] with (cos, sin) of p * theta^(-2i/head_dim) for
+ * p in [0, n_pos), i in [0, head_dim/2), computed in double and rounded to float.
+ * Host-only; theta > 1, head_dim in {64, 128}, n_pos >= 1. */
+ha_status ha_rope_table_fill(double theta, int32_t head_dim, int32_t n_pos, float* host_out);
+
+/* Tile grid used by the attention kernel for this descriptor: block_q query tokens by
+ * block_k keys, n_q_blocks x n_k_blocks tiles from index 0 (last row/column ragged). */
+ha_status ha_tile_shape(const ha_attn_desc* desc, int32_t* block_q, int32_t* block_k,
+                        int32_t* n_q_blocks, int32_t* n_k_blocks);
+
+/* Segment-table tile classifier. Every query row i may attend to a key prefix
+ * [0, lim(i)): causal rows lim = i + 1, full rows lim = seq_len, image (GCA) rows
+ * lim = end of their segment. Writes, on the stream:
+ *   row_limit [batch][seq_len] int32        lim(i)                      (may be NULL)
+ *   ranges    [batch][n_q_blocks][2] int32  (kfull, kend): tiles [0, kfull) are FULL,
+ *                                           [kfull, kend) PARTIAL, the rest SKIP
+ *   labels    [batch][n_q_blocks][n_k_blocks] uint8 ha_tile_label       (may be NULL)
+ * Over the valid part of a tile (rows and keys < seq_len): SKIP = no allowed pair,
+ * FULL = all allowed, PARTIAL = otherwise. All DEVICE pointers, 4-byte aligned
+ * (labels: any alignment). ranges may be NULL only if another output is requested. */
+ha_status ha_classify_tiles(const ha_attn_desc* desc, uint8_t* labels, int32_t* ranges,
+                            int32_t* row_limit, void* stream);
+
+/* Fused q/k RMSNorm + rotary embedding (see ha_prologue_desc). Reads q_in, k_in and
+ * writes q_out, k_out (same layouts and dtype; out may alias in exactly). */
+ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
+                         const void* q_in, const void* k_in, void* q_out, void* k_out,
+                         void* stream);
+
+/* Workspace bytes ha_attn_fwd needs: row limits, tile ranges, and the rotated q and k
+ * when pro is not NULL. */
+size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro);
+
+/* Attention on prepared inputs: q and k already normalised and rotated, row_limit and
+ * ranges from ha_classify_tiles for the same descriptor (so the tile plan can be reused
+ * across layers and denoising steps). out = softmax(scale * q k^T, masked) v per query
+ * head, fp32 accumulation, P rounded to the input dtype for the second product. */
+ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const void* k,
+                              const void* v, const int32_t* row_limit, const int32_t* ranges,
+                              void* out, void* stream);
+
+/* The whole path: classifier, prologue (skipped when pro is NULL: q, k are then used as
+ * given), attention. workspace: DEVICE, 256-byte aligned, >= ha_attn_workspace_bytes. */
+ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
+                      const void* k, const void* v, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HA_ATTN_H */

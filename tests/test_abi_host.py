@@ -1,0 +1,179 @@
+"""C-ABI library on the host, no GPU: it loads, exports what include/ha_attn.h declares,
+and rejects every invalid call with the right status before any HIP call (the device
+pointers below are never dereferenced: validation fails first)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import unified_text_pixel_amd as U
+from unified_text_pixel_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ha_attn.h")
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced in these tests
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:[A-Za-z_][A-Za-z0-9_]*[ *]+)+(ha_[a-z0-9_]+)\(", text,
+                                 flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = U.load_library()
+    names = declared_functions()
+    assert len(names) == 9 and sorted(B.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert U.ha_abi_version() == 1
+
+
+def seg(rows, batch=1):
+    return np.array([rows] * batch, dtype=np.int32)
+
+
+def desc(**kw):
+    base = dict(batch=1, seq_len=80, n_q_heads=4, n_kv_heads=1, head_dim=64, dtype="f32",
+                segments=seg([[0, 16, 0], [16, 64, 1]]))
+    base.update(kw)
+    return U.AttnDesc(**base)
+
+
+BAD_DESCS = [
+    (dict(n_q_heads=6, n_kv_heads=4), B.HA_ERR_INVALID_ARG, "multiple"),
+    (dict(n_q_heads=48, n_kv_heads=3), B.HA_ERR_UNSUPPORTED, "supported: 1, 2, 4, 8"),
+    (dict(head_dim=96), B.HA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(dtype=7), B.HA_ERR_INVALID_ARG, "dtype"),
+    (dict(scale=-1.0), B.HA_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), B.HA_ERR_INVALID_ARG, "scale"),
+    (dict(seq_len=79, segments=seg([[0, 16, 0], [16, 64, 1]])), B.HA_ERR_SEGMENTS, "cover"),
+    (dict(segments=seg([[0, 16, 0], [17, 63, 1]])), B.HA_ERR_SEGMENTS, "starts at"),
+    (dict(segments=seg([[0, 16, 0], [16, 0, 1], [16, 64, 1]])), B.HA_ERR_SEGMENTS, "length"),
+    (dict(segments=seg([[0, 16, 0], [16, 64, 5]])), B.HA_ERR_SEGMENTS, "kind"),
+    (dict(segments=seg([[0, -4, 0], [-4, 84, 1]])), B.HA_ERR_SEGMENTS, "length"),
+    (dict(seq_len=(1 << 22) + 1, segments=seg([[0, (1 << 22) + 1, 0]])), B.HA_ERR_UNSUPPORTED,
+     "exceeds"),
+    (dict(batch=-1), B.HA_ERR_INVALID_ARG, ">= 0"),
+    (dict(n_kv_heads=0), B.HA_ERR_INVALID_ARG, "head counts"),
+]
+
+
+@pytest.mark.parametrize("kw,status,text", BAD_DESCS)
+def test_bad_descriptor_rejected_everywhere(kw, status, text):
+    d = desc(**kw)
+    calls = [
+        lambda: U.ha_tile_shape(d),
+        lambda: U.ha_classify_tiles(d, ranges=FAKE, stream=0),
+        lambda: U.ha_attn_fwd_planned(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
+        lambda: U.ha_attn_fwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0),
+        lambda: U.ha_qk_prologue(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, stream=0),
+    ]
+    for call in calls:
+        with pytest.raises(U.HAError) as e:
+            call()
+        assert e.value.status == status and text in str(e.value), str(e.value)
+    assert U.ha_attn_workspace_bytes(d) == 0
+
+
+def test_bad_pointers_and_workspace():
+    d = desc()
+    with pytest.raises(U.HAError) as e:
+        U.ha_attn_fwd_planned(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.HA_ERR_INVALID_ARG
+    with pytest.raises(U.HAError) as e:
+        U.ha_attn_fwd_planned(d, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.HA_ERR_ALIGNMENT
+    need = U.ha_attn_workspace_bytes(d)
+    assert need > 0 and need % 256 == 0
+    for ws, nbytes in ((None, need), (FAKE + 16, need), (FAKE, need - 1)):
+        with pytest.raises(U.HAError) as e:
+            U.ha_attn_fwd(d, None, FAKE, FAKE, FAKE, FAKE, ws, nbytes, stream=0)
+        assert e.value.status == B.HA_ERR_WORKSPACE
+    with pytest.raises(U.HAError) as e:
+        U.ha_classify_tiles(d, stream=0)
+    assert e.value.status == B.HA_ERR_INVALID_ARG
+
+
+BAD_PROLOGUES = [
+    (dict(rope_kind=9), B.HA_ERR_INVALID_ARG, "rope_kind"),
+    (dict(rope_kind="2d", positions=None, cos_sin=FAKE, n_pos=80), B.HA_ERR_INVALID_ARG, "required"),
+    (dict(rope_kind="2d", positions=FAKE, cos_sin=FAKE, n_pos=0), B.HA_ERR_INVALID_ARG, "n_pos"),
+    (dict(rope_kind="2d", positions=FAKE + 2, cos_sin=FAKE, n_pos=8), B.HA_ERR_ALIGNMENT, "misaligned"),
+    (dict(rope_kind="mrope", positions=FAKE, cos_sin=FAKE, n_pos=8, mrope_sections=(24, 20, 20)),
+     B.HA_ERR_INVALID_ARG, "sum to 32"),
+    (dict(rope_kind="none", q_norm_weight=FAKE), B.HA_ERR_INVALID_ARG, "both"),
+    (dict(rope_kind="none", q_norm_weight=FAKE, k_norm_weight=FAKE, eps=-1.0),
+     B.HA_ERR_INVALID_ARG, "eps"),
+    (dict(rope_kind="none", q_norm_weight=FAKE + 1, k_norm_weight=FAKE), B.HA_ERR_ALIGNMENT,
+     "aligned"),
+]
+
+
+@pytest.mark.parametrize("kw,status,text", BAD_PROLOGUES)
+def test_bad_prologue_rejected(kw, status, text):
+    d = desc()
+    p = U.PrologueDesc(**kw)
+    for call in (lambda: U.ha_qk_prologue(d, p, FAKE, FAKE, FAKE, FAKE, stream=0),
+                 lambda: U.ha_attn_fwd(d, p, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)):
+        with pytest.raises(U.HAError) as e:
+            call()
+        assert e.value.status == status and text in str(e.value), str(e.value)
+
+
+def test_prologue_block_limit():
+    d = desc(n_q_heads=128, n_kv_heads=16, head_dim=128, segments=seg([[0, 80, 0]]))
+    with pytest.raises(U.HAError) as e:
+        U.ha_qk_prologue(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.HA_ERR_UNSUPPORTED
+
+
+def test_empty_work_is_ok_without_launch():
+    for kw in (dict(batch=0, segments=np.zeros((0, 0, 3))), dict(seq_len=0, segments=seg([]))):
+        d = desc(**kw)
+        U.ha_attn_fwd(d, None, None, None, None, None, None, 0, stream=0)
+        U.ha_attn_fwd_planned(d, None, None, None, None, None, None, stream=0)
+        U.ha_classify_tiles(d, ranges=FAKE, stream=0)
+        assert U.ha_last_error() == ""
+
+
+def test_error_text_cleared_by_success():
+    with pytest.raises(U.HAError):
+        U.ha_tile_shape(desc(head_dim=96))
+    assert "head_dim" in U.ha_last_error()
+    U.ha_tile_shape(desc())
+    assert U.ha_last_error() == ""
+
+
+def test_tile_shape():
+    assert U.ha_tile_shape(desc()) == (32, 64, 3, 2)
+    d = desc(batch=2, seq_len=4354, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+             segments=seg([[0, 258, 0], [258, 4096, 1]], 2))
+    assert U.ha_tile_shape(d) == (32, 64, 137, 69)
+    for g, bq in ((1, 128), (2, 64), (8, 32)):
+        d = desc(n_q_heads=8, n_kv_heads=8 // g)
+        assert U.ha_tile_shape(d)[0] == bq
+
+
+def test_rope_table_matches_oracle_angles():
+    for theta, d in ((1e4, 64), (5e6, 128)):
+        t = U.ha_rope_table_fill(theta, d, 300)
+        ang = np.arange(300, dtype=np.float64)[:, None] * oracle.inv_freq(theta, d)[None, :]
+        assert np.allclose(t[..., 0], np.cos(ang), atol=1e-7, rtol=0)
+        assert np.allclose(t[..., 1], np.sin(ang), atol=1e-7, rtol=0)
+    with pytest.raises(U.HAError) as e:
+        U.ha_rope_table_fill(1e4, 100, 10)
+    assert e.value.status == B.HA_ERR_UNSUPPORTED
+    with pytest.raises(U.HAError):
+        U.ha_rope_table_fill(0.5, 64, 10)
+
+
+def test_workspace_layout():
+    d = desc(batch=2, seq_len=4354, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+             segments=seg([[0, 258, 0], [258, 4096, 1]], 2))
+    plain = U.ha_attn_workspace_bytes(d)
+    with_pro = U.ha_attn_workspace_bytes(d, U.PrologueDesc("none"))
+    assert plain >= 2 * 4354 * 4 + 2 * 137 * 8
+    assert with_pro - plain >= 2 * 4354 * 40 * 128 * 2

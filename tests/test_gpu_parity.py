@@ -1,0 +1,279 @@
+"""HIP path against the oracle, through the C ABI, on seeded inputs.
+
+Small cases compare every output element; the five full-size workloads compare sampled
+rows (all heads) that the oracle computes one by one, in the launch configuration the
+benchmark times, plus properties that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import (compare, desc_for, f64, prologue_for, refresh_bits, require_gpu,
+                         run_fwd, sample_rows)
+from unified_text_pixel_amd import api, binding as B
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+C, F, G = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def small(segs, hq=8, hkv=2, d=128, rope="mrope", sections=None, norm=True, batch=2,
+          dtype="bf16", theta=5e6, seed=21):
+    if sections is None:
+        sections = (24, 20, 20) if d == 128 else (12, 10, 10)
+    return W.Workload(name="small", description="", batch=batch, segments=tuple(segs),
+                      n_q_heads=hq, n_kv_heads=hkv, head_dim=d, dtype=dtype, rope=rope,
+                      rope_theta=theta, mrope_sections=sections, qk_norm=norm, norm_eps=1e-6,
+                      seed=seed)
+
+
+SMALL = {
+    # HiDream-style: causal prefix (ragged vs the 64-key tile) then a full grid
+    "hd_small": small([W.Segment(C, 70), W.Segment(F, 256, (16, 16))]),
+    # editing layout: text, full generation, causal reference; S not a tile multiple
+    "edit_small": small([W.Segment(C, 40), W.Segment(F, 100, (10, 10)), W.Segment(C, 81, (9, 9))]),
+    # HunyuanImage-style interleave with adjacent image segments, 2D rotary, no q/k norm
+    "gca_small": small([W.Segment(C, 33), W.Segment(G, 64, (8, 8)), W.Segment(G, 49, (7, 7)),
+                        W.Segment(C, 17), W.Segment(G, 100, (10, 10)), W.Segment(C, 5)],
+                       rope="2d", norm=False, theta=1e4),
+    "mha_g1": small([W.Segment(C, 50), W.Segment(F, 150)], hq=2, hkv=2, rope="1d"),
+    "gqa_g2": small([W.Segment(C, 50), W.Segment(F, 150)], hq=4, hkv=2, rope="1d"),
+    "gqa_g8": small([W.Segment(F, 90), W.Segment(C, 111)], hq=16, hkv=2, rope="none", norm=True),
+    "d64_bf16": small([W.Segment(C, 45), W.Segment(G, 81, (9, 9)), W.Segment(C, 3)], d=64,
+                      rope="mrope"),
+    "one_token": small([W.Segment(C, 1)], batch=3),
+    "all_causal": small([W.Segment(C, 300)], rope="1d"),
+    "all_full": small([W.Segment(F, 200)], rope="2d", theta=1e4),
+    "f32_mixed": small([W.Segment(C, 20), W.Segment(F, 36, (6, 6)), W.Segment(G, 25, (5, 5))],
+                       dtype="f32", hq=4, hkv=1, d=64, rope="2d", theta=1e4),
+    "f32_d128": small([W.Segment(C, 30), W.Segment(F, 70)], dtype="f32", hq=8, hkv=2, d=128,
+                      rope="mrope"),
+}
+
+
+# ---------------------------------------------------------------- classifier
+def classify(w, segments=None):
+    desc = desc_for(w, segments)
+    bq, bk, nq, nk = B.ha_tile_shape(desc)
+    labels = torch.empty((w.batch, nq, nk), dtype=torch.uint8, device="cuda")
+    ranges = torch.empty((w.batch, nq, 2), dtype=torch.int32, device="cuda")
+    lim = torch.empty((w.batch, w.seq_len), dtype=torch.int32, device="cuda")
+    B.ha_classify_tiles(desc, labels, ranges, lim)
+    torch.cuda.synchronize()
+    return (bq, bk), labels.cpu().numpy(), ranges.cpu().numpy(), lim.cpu().numpy()
+
+
+def check_labels(w, segments):
+    (bq, bk), labels, ranges, lim = classify(w, segments)
+    for b in range(w.batch):
+        M = oracle.explicit_mask(segments[b], w.seq_len)
+        want = oracle.tile_labels(M, bq, bk)
+        assert np.array_equal(labels[b], want), f"batch {b}: tile labels differ"
+        assert np.array_equal(lim[b], M.sum(axis=1)), f"batch {b}: row limits differ"
+        kfull = (want == 1).sum(axis=1)
+        kend = want.shape[1] - (want == 0).sum(axis=1)
+        assert np.array_equal(ranges[b, :, 0], kfull) and np.array_equal(ranges[b, :, 1], kend)
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_classifier_bit_exact_configs(name):
+    w = W.get_config(name)
+    check_labels(w, W.segment_table(w))
+
+
+def test_classifier_bit_exact_random_layouts():
+    rng = np.random.default_rng(5)
+    for trial in range(25):
+        n = int(rng.integers(1, 9))
+        batch = int(rng.integers(1, 4))
+        S = int(rng.integers(n, 700))
+        tables = []
+        for b in range(batch):
+            cuts = np.sort(rng.choice(np.arange(1, S), size=n - 1, replace=False)) if n > 1 else []
+            bounds = [0, *cuts, S]
+            kinds = rng.integers(0, 3, size=n)
+            tables.append([[bounds[s], bounds[s + 1] - bounds[s], kinds[s]] for s in range(n)])
+        seg = np.array(tables, dtype=np.int32)
+        w = small([W.Segment(C, S)], batch=batch, hq=[8, 4, 16, 2][trial % 4], hkv=2)
+        check_labels(w, seg)
+
+
+def test_classifier_many_batch_items():
+    # more segment rows than one launch's kernel arguments hold: several launches
+    w = small([W.Segment(C, 10), W.Segment(G, 30), W.Segment(F, 25)], batch=50)
+    seg = W.segment_table(w)
+    seg[1::3, 1:, 2] = [F, G]
+    check_labels(w, seg)
+
+
+# ---------------------------------------------------------------- prologue
+@pytest.mark.parametrize("name", ["hd_small", "gca_small", "d64_bf16", "f32_mixed", "f32_d128"])
+def test_prologue_parity(name):
+    w = SMALL[name]
+    x = W.generate(w)
+    dev = to_device(x)
+    desc, pro = desc_for(w), prologue_for(w, dev)
+    qo, ko = torch.empty_like(dev["q"]), torch.empty_like(dev["k"])
+    B.ha_qk_prologue(desc, pro, dev["q"], dev["k"], qo, ko)
+    torch.cuda.synchronize()
+    q_ref, k_ref = oracle.prologue(x)
+    for got, want in ((f64(qo), q_ref), (f64(ko), k_ref)):
+        if w.dtype == "bf16":  # one bf16 rounding of an fp32 result: within 1 ulp (2^-7 relative)
+            assert (np.abs(got - want) <= 2.0 ** -7 * np.abs(want) + 1e-6).all()
+        else:
+            assert np.abs(got - want).max() <= 1e-5 * np.abs(want).max()
+
+
+@pytest.mark.parametrize("name", ["hd1024", "hunyuan"])
+def test_prologue_parity_full_size_in_place(name):
+    w = W.get_config(name)
+    x = W.generate(w)
+    dev = to_device(x)
+    desc, pro = desc_for(w), prologue_for(w, dev)
+    B.ha_qk_prologue(desc, pro, dev["q"], dev["k"], dev["q"], dev["k"])  # aliasing allowed
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, w.seq_len, size=64)
+    sub = W.Inputs(workload=w.replace(batch=1), q=x.q[:1, rows], k=x.k[:1, rows], v=x.v[:1, rows],
+                   q_bits=None, k_bits=None, v_bits=None, w_q=x.w_q, w_k=x.w_k,
+                   positions=x.positions[:1, rows], segments=x.segments[:1])
+    q_ref, k_ref = oracle.prologue(sub)
+    for got, want in ((f64(dev["q"][0, rows]), q_ref[0]), (f64(dev["k"][0, rows]), k_ref[0])):
+        assert (np.abs(got - want) <= 2.0 ** -7 * np.abs(want) + 1e-6).all()
+
+
+# ---------------------------------------------------------------- attention
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attention_parity_small(name):
+    w = SMALL[name]
+    x = W.generate(w)
+    out, _ = run_fwd(x)
+    compare(f64(out), oracle.hot_path(x), w.dtype, name)
+
+
+def test_tiny_config_fp32():
+    w = W.get_config("tiny")
+    x = W.generate(w)
+    out, _ = run_fwd(x)
+    compare(f64(out), oracle.hot_path(x), "f32", "tiny")
+
+
+@pytest.mark.parametrize("name", ["hd1024", "hd2048", "edit", "hunyuan"])
+def test_full_size_sampled_rows(name):
+    w = W.get_config(name)
+    x = W.generate(w)
+    out, dev = run_fwd(x)
+    got = f64(out)
+    rows = sample_rows(w)
+    heads = list(range(w.n_q_heads))
+    errs = []
+    for b in range(w.batch):
+        want = oracle.hot_path_rows(x, b, rows, heads)
+        errs.append(np.abs(got[b, rows] - want))
+        compare(got[b, rows], want, w.dtype, f"{name} batch {b} ({len(rows)} rows x {len(heads)} heads)")
+    # row 0 is causal text: it attends only to itself, so its output is v_0 exactly
+    v0 = f64(dev["v"][:, 0])
+    assert np.array_equal(got[:, 0], np.repeat(v0, w.n_q_heads // w.n_kv_heads, axis=1))
+
+
+def uniform_probe(w):
+    """q = 0 makes every allowed weight exactly 1 (RMSNorm and rotary of 0 are 0), masked
+    ones exactly 0; with v_j one-hot on channel (j // 64) mod d the output channel c of row
+    i is the count of allowed keys in the 64-key blocks on c, over lim(i)."""
+    x = W.generate(w)
+    x.q[:] = 0.0
+    S, d = w.seq_len, w.head_dim
+    x.v[:] = 0.0
+    chan = (np.arange(S) // 64) % d
+    x.v[:, np.arange(S), :, chan] = 1.0
+    out, _ = run_fwd(refresh_bits(x))
+    got = f64(out)
+    for b in range(w.batch):
+        lim = oracle.explicit_mask(x.segments[b], S).sum(axis=1)
+        for i in np.unique(np.r_[np.arange(0, S, 7), S - 1]):
+            want = np.bincount(chan[:lim[i]], minlength=d) / lim[i]
+            tol = 2.0 ** -7 * want + 1e-7
+            assert (np.abs(got[b, i] - want[None, :]) <= tol).all(), (w.name, b, i)
+
+
+@pytest.mark.parametrize("name", ["hd2048", "edit", "hunyuan"])
+def test_uniform_probe_full_size(name):
+    uniform_probe(W.get_config(name))
+
+
+@pytest.mark.parametrize("name", ["hd_small", "edit_small", "gca_small", "all_full"])
+def test_uniform_probe_small(name):
+    uniform_probe(SMALL[name])
+
+
+def test_future_tokens_do_not_leak():
+    w = SMALL["gca_small"].replace(batch=1)
+    x = W.generate(w)
+    base, _ = run_fwd(x)
+    # segments: C[0,33) G[33,97) G[97,146) C[146,163) G[163,263) C[263,268)
+    y = W.generate(w)
+    y.q[0, 120:] += 1.0
+    y.k[0, 120:] += 1.0
+    y.v[0, 120:] += 1.0
+    pert, _ = run_fwd(refresh_bits(y))
+    b0, p0 = base.cpu(), pert.cpu()
+    assert torch.equal(b0[0, :97], p0[0, :97])          # rows that end before token 120
+    assert not torch.equal(b0[0, 97:120], p0[0, 97:120])  # image rows see their whole segment
+
+
+def test_deterministic_and_fwd_equals_planned():
+    w = SMALL["edit_small"]
+    x = W.generate(w)
+    a, dev = run_fwd(x)
+    b, _ = run_fwd(x, dev)
+    assert torch.equal(a, b)
+    desc, pro = desc_for(w), prologue_for(w, dev)
+    bq, bk, nq, nk = B.ha_tile_shape(desc)
+    ranges = torch.empty((w.batch, nq, 2), dtype=torch.int32, device="cuda")
+    lim = torch.empty((w.batch, w.seq_len), dtype=torch.int32, device="cuda")
+    B.ha_classify_tiles(desc, None, ranges, lim)
+    qr, kr = torch.empty_like(dev["q"]), torch.empty_like(dev["k"])
+    B.ha_qk_prologue(desc, pro, dev["q"], dev["k"], qr, kr)
+    out = torch.empty_like(dev["q"])
+    B.ha_attn_fwd_planned(desc, qr, kr, dev["v"], lim, ranges, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, a)
+
+
+def test_per_batch_layouts_differ():
+    w = small([W.Segment(C, 40), W.Segment(F, 60), W.Segment(G, 28)], batch=3)
+    seg = W.segment_table(w)
+    seg[1] = [[0, 100, F], [100, 10, C], [110, 18, G]]
+    seg[2] = [[0, 1, C], [1, 64, G], [65, 63, G]]
+    x = W.generate(w)
+    x.segments = seg
+    out, _ = run_fwd(x)
+    compare(f64(out), oracle.hot_path(x), "bf16", "per-batch layouts")
+
+
+def test_empty_inputs_launch_nothing():
+    for b, s in ((0, 100), (2, 0)):
+        desc = B.AttnDesc(b, s, 8, 2, 128, "bf16", np.zeros((b, 1, 3)) if b else [])
+        B.ha_attn_fwd(desc, None, None, None, None, None, None, 0)
+        B.ha_classify_tiles(desc, ranges=torch.empty(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_api_layer_matches_abi():
+    w = SMALL["hd_small"]
+    x = W.generate(w)
+    ref, dev = run_fwd(x)
+    cs = api.rope_table(w.rope_theta, w.head_dim, w.seq_len)
+    out = api.hybrid_attention(dev["q"], dev["k"], dev["v"], x.segments, rope=w.rope,
+                               positions=dev["positions"], cos_sin=cs,
+                               mrope_sections=w.mrope_sections, q_norm_weight=dev["w_q"],
+                               k_norm_weight=dev["w_k"], eps=w.norm_eps)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

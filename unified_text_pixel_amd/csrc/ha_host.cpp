@@ -1,0 +1,396 @@
+// C-ABI entry points: host-side validation (before any HIP call), workspace layout and
+// kernel dispatch. The declarations and the contract are in include/ha_attn.h.
+//
+// Validation follows the convention of the hidream-o1-p100a model card ("Serving (HTTP)":
+// contract errors are rejected without touching the card): every check runs on the host
+// and a failed check returns before the device or the stream is used.
+#include "ha_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "ha_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ha_status fail(ha_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ha_status ok() {
+  g_last_error.clear();
+  return HA_OK;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("HA_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+ha_status check_launch(hipError_t e, hipStream_t stream, const char* what) {
+  if (e != hipSuccess) return fail(HA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  if (debug_sync()) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(HA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+  }
+  return HA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- descriptor checks
+ha_status check_desc(const ha_attn_desc* d) {
+  if (!d) return fail(HA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 0 || d->seq_len < 0)
+    return fail(HA_ERR_INVALID_ARG, "batch (%d) and seq_len (%d) must be >= 0", d->batch, d->seq_len);
+  if (d->seq_len > HA_MAX_SEQ_LEN)
+    return fail(HA_ERR_UNSUPPORTED, "seq_len %d exceeds %d", d->seq_len, HA_MAX_SEQ_LEN);
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(HA_ERR_INVALID_ARG, "head counts must be >= 1 (got %d, %d)", d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(HA_ERR_INVALID_ARG, "n_q_heads %d is not a multiple of n_kv_heads %d", d->n_q_heads,
+                d->n_kv_heads);
+  const int group = d->n_q_heads / d->n_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(HA_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads = %d; supported: 1, 2, 4, 8", group);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(HA_ERR_UNSUPPORTED, "head_dim %d; supported: 64, 128", d->head_dim);
+  if (d->dtype != HA_DTYPE_BF16 && d->dtype != HA_DTYPE_F32)
+    return fail(HA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (!std::isfinite(d->scale) || d->scale < 0.f)
+    return fail(HA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if ((int64_t)d->n_q_heads * d->head_dim * (int64_t)d->seq_len * (d->batch ? d->batch : 1) >
+      (int64_t(1) << 40))
+    return fail(HA_ERR_UNSUPPORTED, "tensor too large");
+  if (d->batch == 0 || d->seq_len == 0) return HA_OK;  // empty: segments not consulted
+  if (!d->segments) return fail(HA_ERR_INVALID_ARG, "segments is NULL");
+  if (d->n_segments < 1 || d->n_segments > HA_MAX_SEGMENTS)
+    return fail(HA_ERR_SEGMENTS, "n_segments %d outside [1, %d]", d->n_segments, HA_MAX_SEGMENTS);
+  for (int b = 0; b < d->batch; ++b) {
+    int64_t at = 0;
+    for (int s = 0; s < d->n_segments; ++s) {
+      const ha_segment& g = d->segments[(int64_t)b * d->n_segments + s];
+      if (g.kind != HA_SEG_CAUSAL && g.kind != HA_SEG_FULL && g.kind != HA_SEG_GCA)
+        return fail(HA_ERR_SEGMENTS, "batch %d segment %d: unknown kind %d", b, s, g.kind);
+      if (g.length <= 0)
+        return fail(HA_ERR_SEGMENTS, "batch %d segment %d: length %d must be > 0", b, s, g.length);
+      if (g.start != at)
+        return fail(HA_ERR_SEGMENTS, "batch %d segment %d: starts at %d, expected %lld", b, s, g.start,
+                    (long long)at);
+      at += g.length;
+    }
+    if (at != d->seq_len)
+      return fail(HA_ERR_SEGMENTS, "batch %d: segments cover %lld tokens, seq_len is %d", b, (long long)at,
+                  d->seq_len);
+  }
+  return HA_OK;
+}
+
+bool empty(const ha_attn_desc* d) { return d->batch == 0 || d->seq_len == 0; }
+
+ha_status check_tensor(const void* p, const char* name) {
+  if (!p) return fail(HA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(HA_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return HA_OK;
+}
+
+int n_axes_of(int rope_kind) { return rope_kind == HA_ROPE_2D ? 2 : (rope_kind == HA_ROPE_MROPE ? 3 : 1); }
+
+ha_status check_prologue(const ha_attn_desc* d, const ha_prologue_desc* p) {
+  if (!p) return fail(HA_ERR_INVALID_ARG, "prologue desc is NULL");
+  if (p->rope_kind < HA_ROPE_NONE || p->rope_kind > HA_ROPE_MROPE)
+    return fail(HA_ERR_INVALID_ARG, "unknown rope_kind %d", p->rope_kind);
+  if (p->rope_kind == HA_ROPE_MROPE) {
+    const int* s = p->mrope_sections;
+    if (s[0] < 0 || s[1] < 0 || s[2] < 0 || s[0] + s[1] + s[2] != d->head_dim / 2)
+      return fail(HA_ERR_INVALID_ARG, "mrope_sections (%d, %d, %d) must be >= 0 and sum to %d", s[0], s[1],
+                  s[2], d->head_dim / 2);
+  }
+  if (p->rope_kind != HA_ROPE_NONE) {
+    if (!p->positions || !p->cos_sin) return fail(HA_ERR_INVALID_ARG, "positions and cos_sin are required");
+    if (!aligned(p->positions, 4) || !aligned(p->cos_sin, 8))
+      return fail(HA_ERR_ALIGNMENT, "positions (4) or cos_sin (8) misaligned");
+    if (p->n_pos < 1) return fail(HA_ERR_INVALID_ARG, "n_pos must be >= 1");
+  }
+  if ((p->q_norm_weight == nullptr) != (p->k_norm_weight == nullptr))
+    return fail(HA_ERR_INVALID_ARG, "q_norm_weight and k_norm_weight must both be set or both NULL");
+  if (p->q_norm_weight) {
+    if (!aligned(p->q_norm_weight, 4) || !aligned(p->k_norm_weight, 4))
+      return fail(HA_ERR_ALIGNMENT, "norm weights must be 4-byte aligned");
+    if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(HA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  }
+  if ((d->n_q_heads + d->n_kv_heads) * (d->head_dim / 16) > 1024)
+    return fail(HA_ERR_UNSUPPORTED, "prologue: (n_q_heads + n_kv_heads) * head_dim / 16 must be <= 1024");
+  return HA_OK;
+}
+
+void tile_shape(const ha_attn_desc* d, int* bq, int* bk, int* nq, int* nk) {
+  *bq = ha::attn_block_q(d->head_dim, d->n_q_heads / d->n_kv_heads, d->dtype == HA_DTYPE_F32);
+  *bk = ha::kBlockK;
+  *nq = (int)cdiv(d->seq_len, *bq);
+  *nk = (int)cdiv(d->seq_len, *bk);
+}
+
+// Launch the classifier over batch chunks whose segment tables fit the kernel arguments.
+ha_status run_classify(const ha_attn_desc* d, uint8_t* labels, int32_t* ranges, int32_t* row_limit,
+                       hipStream_t stream) {
+  ha::ClassifyArgs a{};
+  int bq, bk, nq, nk;
+  tile_shape(d, &bq, &bk, &nq, &nk);
+  a.S = d->seq_len;
+  a.nq = nq;
+  a.nk = nk;
+  a.bq = bq;
+  a.bk = bk;
+  a.labels = labels;
+  a.ranges = ranges;
+  a.row_limit = row_limit;
+  const int per_launch = ha::kArgSegs / d->n_segments;
+  for (int b0 = 0; b0 < d->batch; b0 += per_launch) {
+    const int n = std::min(per_launch, d->batch - b0);
+    a.seg.n_items = n;
+    a.seg.b0 = b0;
+    a.seg.n_seg = d->n_segments;
+    for (int t = 0; t < n * d->n_segments; ++t) {
+      const ha_segment& g = d->segments[(int64_t)b0 * d->n_segments + t];
+      a.seg.start[t] = g.start;
+      a.seg.end[t] = g.start + g.length;
+      a.seg.kind[t] = g.kind;
+    }
+    ha_status st = check_launch(ha::launch_classify(a, stream), stream, "classifier");
+    if (st != HA_OK) return st;
+  }
+  return HA_OK;
+}
+
+void axis_table(const ha_prologue_desc* p, int head_dim, uint8_t* axis) {
+  const int half = head_dim / 2;
+  if (p->rope_kind == HA_ROPE_2D) {
+    for (int i = 0; i < half; ++i) axis[i] = (uint8_t)(i & 1);
+  } else if (p->rope_kind == HA_ROPE_MROPE) {
+    // deal pairs to T, H, W in turn; an axis leaves the rotation once it holds its count
+    int left[3] = {p->mrope_sections[0], p->mrope_sections[1], p->mrope_sections[2]};
+    int ax = 0;
+    for (int i = 0; i < half;) {
+      if (left[ax] > 0) {
+        axis[i++] = (uint8_t)ax;
+        --left[ax];
+      }
+      ax = (ax + 1) % 3;
+    }
+  } else {
+    for (int i = 0; i < half; ++i) axis[i] = 0;
+  }
+}
+
+ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const void* q_in, const void* k_in,
+                       void* q_out, void* k_out, hipStream_t stream) {
+  ha::PrologueArgs a{};
+  a.q_in = q_in;
+  a.k_in = k_in;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.rotate = p->rope_kind != HA_ROPE_NONE;
+  a.positions = a.rotate ? p->positions : nullptr;
+  a.cos_sin = a.rotate ? p->cos_sin : nullptr;
+  a.wq = p->q_norm_weight;
+  a.wk = p->k_norm_weight;
+  a.B = d->batch;
+  a.S = d->seq_len;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.D = d->head_dim;
+  a.n_axes = n_axes_of(p->rope_kind);
+  a.n_pos = p->n_pos;
+  a.eps = p->eps;
+  a.f32 = d->dtype == HA_DTYPE_F32;
+  axis_table(p, d->head_dim, a.axis);
+  return check_launch(ha::launch_prologue(a, stream), stream, "prologue");
+}
+
+ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const void* v, const int32_t* row_limit,
+                   const int32_t* ranges, void* out, hipStream_t stream) {
+  ha::AttnArgs a{};
+  int bq, bk, nq, nk;
+  tile_shape(d, &bq, &bk, &nq, &nk);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.row_limit = row_limit;
+  a.ranges = ranges;
+  a.B = d->batch;
+  a.S = d->seq_len;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.D = d->head_dim;
+  a.nq = nq;
+  const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / std::sqrt((double)d->head_dim);
+  a.scale_log2e = (float)(scale * 1.4426950408889634074);
+  a.f32 = d->dtype == HA_DTYPE_F32;
+  return check_launch(ha::launch_attn(a, stream), stream, "attention");
+}
+
+struct Workspace {
+  size_t row_limit, ranges, q_rot, k_rot, total;
+};
+
+Workspace workspace_layout(const ha_attn_desc* d, bool prologue) {
+  int bq, bk, nq, nk;
+  tile_shape(d, &bq, &bk, &nq, &nk);
+  const size_t elem = d->dtype == HA_DTYPE_F32 ? 4 : 2;
+  Workspace w{};
+  size_t at = 0;
+  w.row_limit = at;
+  at = round256(at + (size_t)d->batch * d->seq_len * 4);
+  w.ranges = at;
+  at = round256(at + (size_t)d->batch * nq * 2 * 4);
+  if (prologue) {
+    w.q_rot = at;
+    at = round256(at + (size_t)d->batch * d->seq_len * d->n_q_heads * d->head_dim * elem);
+    w.k_rot = at;
+    at = round256(at + (size_t)d->batch * d->seq_len * d->n_kv_heads * d->head_dim * elem);
+  }
+  w.total = at;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ha_abi_version(void) { return HA_ABI_VERSION; }
+
+const char* ha_last_error(void) { return g_last_error.c_str(); }
+
+ha_status ha_rope_table_fill(double theta, int32_t head_dim, int32_t n_pos, float* host_out) {
+  if (!host_out) return fail(HA_ERR_INVALID_ARG, "host_out is NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(HA_ERR_UNSUPPORTED, "head_dim %d; supported: 64, 128", head_dim);
+  if (n_pos < 1) return fail(HA_ERR_INVALID_ARG, "n_pos must be >= 1");
+  if (!(theta > 1.0) || !std::isfinite(theta)) return fail(HA_ERR_INVALID_ARG, "theta must be finite and > 1");
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    const double f = std::pow(theta, -2.0 * i / head_dim);
+    for (int64_t p = 0; p < n_pos; ++p) {
+      const double ang = (double)p * f;
+      host_out[(p * half + i) * 2 + 0] = (float)std::cos(ang);
+      host_out[(p * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  }
+  return ok();
+}
+
+ha_status ha_tile_shape(const ha_attn_desc* desc, int32_t* block_q, int32_t* block_k, int32_t* n_q_blocks,
+                        int32_t* n_k_blocks) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if (!block_q || !block_k || !n_q_blocks || !n_k_blocks) return fail(HA_ERR_INVALID_ARG, "output pointer is NULL");
+  int bq, bk, nq, nk;
+  tile_shape(desc, &bq, &bk, &nq, &nk);
+  *block_q = bq;
+  *block_k = bk;
+  *n_q_blocks = nq;
+  *n_k_blocks = nk;
+  return ok();
+}
+
+ha_status ha_classify_tiles(const ha_attn_desc* desc, uint8_t* labels, int32_t* ranges, int32_t* row_limit,
+                            void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if (!labels && !ranges && !row_limit) return fail(HA_ERR_INVALID_ARG, "no output requested");
+  if ((ranges && !aligned(ranges, 4)) || (row_limit && !aligned(row_limit, 4)))
+    return fail(HA_ERR_ALIGNMENT, "ranges and row_limit must be 4-byte aligned");
+  if (empty(desc)) return ok();
+  st = run_classify(desc, labels, ranges, row_limit, static_cast<hipStream_t>(stream));
+  return st == HA_OK ? ok() : st;
+}
+
+ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q_in, const void* k_in,
+                         void* q_out, void* k_out, void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if ((st = check_prologue(desc, pro)) != HA_OK) return st;
+  if (empty(desc)) return ok();
+  if ((st = check_tensor(q_in, "q_in")) != HA_OK || (st = check_tensor(k_in, "k_in")) != HA_OK ||
+      (st = check_tensor(q_out, "q_out")) != HA_OK || (st = check_tensor(k_out, "k_out")) != HA_OK)
+    return st;
+  st = run_prologue(desc, pro, q_in, k_in, q_out, k_out, static_cast<hipStream_t>(stream));
+  return st == HA_OK ? ok() : st;
+}
+
+size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro) {
+  if (check_desc(desc) != HA_OK) return 0;
+  return workspace_layout(desc, pro != nullptr).total;
+}
+
+ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const void* k, const void* v,
+                              const int32_t* row_limit, const int32_t* ranges, void* out, void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if (empty(desc)) return ok();
+  if ((st = check_tensor(q, "q")) != HA_OK || (st = check_tensor(k, "k")) != HA_OK ||
+      (st = check_tensor(v, "v")) != HA_OK || (st = check_tensor(out, "out")) != HA_OK)
+    return st;
+  if (!row_limit || !ranges) return fail(HA_ERR_INVALID_ARG, "row_limit and ranges are required");
+  if (!aligned(row_limit, 4) || !aligned(ranges, 4))
+    return fail(HA_ERR_ALIGNMENT, "row_limit and ranges must be 4-byte aligned");
+  st = run_attn(desc, q, k, v, row_limit, ranges, out, static_cast<hipStream_t>(stream));
+  return st == HA_OK ? ok() : st;
+}
+
+ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
+                      const void* v, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if (pro && (st = check_prologue(desc, pro)) != HA_OK) return st;
+  if (empty(desc)) return ok();
+  if ((st = check_tensor(q, "q")) != HA_OK || (st = check_tensor(k, "k")) != HA_OK ||
+      (st = check_tensor(v, "v")) != HA_OK || (st = check_tensor(out, "out")) != HA_OK)
+    return st;
+  const Workspace w = workspace_layout(desc, pro != nullptr);
+  if (!workspace) return fail(HA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(HA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* row_limit = reinterpret_cast<int32_t*>(ws + w.row_limit);
+  int32_t* ranges = reinterpret_cast<int32_t*>(ws + w.ranges);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_classify(desc, nullptr, ranges, row_limit, s)) != HA_OK) return st;
+  const void* qa = q;
+  const void* ka = k;
+  if (pro) {
+    void* qr = ws + w.q_rot;
+    void* kr = ws + w.k_rot;
+    if ((st = run_prologue(desc, pro, q, k, qr, kr, s)) != HA_OK) return st;
+    qa = qr;
+    ka = kr;
+  }
+  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, s);
+  return st == HA_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Fused q/k RMSNorm + rotary embedding, bound by HBM bandwidth.
+//
+// Per head row x of length D (hidream-o1-p100a model card, "q/k RMSNorm" and "3-axis
+// interleaved mRoPE [24,20,20]"; HunyuanImage 3.0 digest, "Generalized 2D Rotary
+// Position Embedding"):
+//   y = x / sqrt(mean(x^2) + eps) * w                         (when weights are given)
+//   (y[i], y[i+D/2]) <- rotation of the pair by pos[axis(i)] * theta^(-2i/D)
+// Every head of a token shares the token's angles, so one workgroup handles one token:
+// it gathers the token's D/2 (cos, sin) pairs from the table into LDS once, then D/16
+// threads per head row each own 8 pairs, i.e. elements [8c, 8c+8) and [D/2+8c, D/2+8c+8),
+// which are 16-byte (bf16) loads and stores. The row's mean square is reduced across
+// those D/16 lanes. fp32 math throughout; bf16 results are rounded to nearest even.
+#include "ha_internal.h"
+
+namespace ha {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool F32>
+__device__ inline void load8(const void* base, int64_t off, float* x) {
+  if constexpr (F32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off);
+    f32x4 a = p[0], b = p[1];
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+  } else {
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(base) + off);
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
+  }
+}
+
+template <bool F32>
+__device__ inline void store8(void* base, int64_t off, const float* x) {
+  if constexpr (F32) {
+    f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(base) + off);
+    p[0] = f32x4{x[0], x[1], x[2], x[3]};
+    p[1] = f32x4{x[4], x[5], x[6], x[7]};
+  } else {
+    bf16x8 v;
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(x[e]);
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(base) + off) = v;
+  }
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(1024) void prologue_kernel(PrologueArgs a) {
+  constexpr int HALF = D / 2;
+  constexpr int TPR = D / 16;  // threads per head row
+  __shared__ float2 cs[HALF];
+  const int64_t token = blockIdx.x;  // b * S + s
+
+  if (a.rotate) {
+    for (int t = threadIdx.x; t < HALF; t += blockDim.x) {
+      int p = a.positions[token * a.n_axes + a.axis[t]];
+      p = min(max(p, 0), a.n_pos - 1);
+      cs[t] = reinterpret_cast<const float2*>(a.cos_sin)[(int64_t)p * HALF + t];
+    }
+  }
+  __syncthreads();
+
+  const int row = threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= a.Hq + a.Hkv) return;  // whole rows drop out together
+  const bool isq = row < a.Hq;
+  const int h = isq ? row : row - a.Hq;
+  const int64_t base = (token * (isq ? a.Hq : a.Hkv) + h) * D;
+  const void* in = isq ? a.q_in : a.k_in;
+  void* out = isq ? a.q_out : a.k_out;
+  const float* w = isq ? a.wq : a.wk;
+
+  float x1[8], x2[8];
+  load8<F32>(in, base + 8 * c, x1);
+  load8<F32>(in, base + HALF + 8 * c, x2);
+
+  if (w) {
+    float ss = 0.f;
+    for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+    for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o);
+    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+    for (int e = 0; e < 8; ++e) {
+      x1[e] = x1[e] * inv * w[8 * c + e];
+      x2[e] = x2[e] * inv * w[HALF + 8 * c + e];
+    }
+  }
+  if (a.rotate) {
+    for (int e = 0; e < 8; ++e) {
+      const float2 t = cs[8 * c + e];
+      const float y1 = x1[e] * t.x - x2[e] * t.y;
+      const float y2 = x2[e] * t.x + x1[e] * t.y;
+      x1[e] = y1;
+      x2[e] = y2;
+    }
+  }
+  store8<F32>(out, base + 8 * c, x1);
+  store8<F32>(out, base + HALF + 8 * c, x2);
+}
+
+template <int D, bool F32>
+hipError_t launch(const PrologueArgs& a, hipStream_t stream) {
+  const int threads = ((a.Hq + a.Hkv) * (D / 16) + 63) / 64 * 64;
+  hipLaunchKernelGGL((prologue_kernel<D, F32>), dim3((unsigned)((int64_t)a.B * a.S)),
+                     dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
+  if (a.D == 128) return a.f32 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+  return a.f32 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+}
+
+}  // namespace ha

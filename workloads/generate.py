@@ -73,7 +73,7 @@ def positions_for(w: Workload) -> np.ndarray:
                 pos[s0:s0 + seg.length, 1] = s0 + r
                 pos[s0:s0 + seg.length, 2] = s0 + c
         s0 += seg.length
-    return np.ascontiguousarray(np.broadcast_to(pos, (w.batch, S, A)))
+    return np.broadcast_to(pos, (w.batch, S, A)).copy()
 
 
 @dataclass
