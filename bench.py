@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--workload", default="hd2048")
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -115,11 +117,14 @@ def main():
     print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
     x = W.generate(w)
     dev = to_device(x)
+    # the prologue writes q prescaled by softmax scale * log2(e), which the attention
+    # kernel then takes as is (q_prescaled = 1): the same path ha_attn_fwd runs
     desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype,
-                      x.segments)
+                      x.segments, q_prescaled=1)
     cs = api.rope_table(w.rope_theta, w.head_dim, w.seq_len) if w.rope != "none" else None
     pro = B.PrologueDesc(w.rope, dev["positions"], cs, 0 if cs is None else cs.shape[0],
-                         dev["w_q"], dev["w_k"], w.norm_eps, w.mrope_sections)
+                         dev["w_q"], dev["w_k"], w.norm_eps, w.mrope_sections,
+                         q_out_scale=B.ha_q_prescale(desc))
     bq, bk, nq, nk = B.ha_tile_shape(desc)
     sets = []
     for _ in range(args.sets):
@@ -146,6 +151,13 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()

@@ -82,6 +82,9 @@ typedef struct {
   const ha_segment* segments; /* HOST memory, [batch][n_segments] */
   int32_t n_segments;       /* 1 .. HA_MAX_SEGMENTS (per batch item) */
   float scale;              /* softmax scale; 0 means 1 / sqrt(head_dim) */
+  int32_t q_prescaled;      /* ha_attn_fwd_planned only: 1 when q already carries the factor
+                               scale * log2(e) (ha_qk_prologue with q_out_scale set to
+                               ha_q_prescale(desc)), 0 for plain q */
 } ha_attn_desc;
 
 /* q/k prologue: RMSNorm over head_dim (y = x / sqrt(mean(x^2) + eps) * w, before the
@@ -103,6 +106,7 @@ typedef struct {
   const float* q_norm_weight;   /* DEVICE fp32 [head_dim], or NULL for no RMSNorm */
   const float* k_norm_weight;   /* DEVICE fp32 [head_dim]; NULL exactly when q's is */
   float eps;                    /* RMSNorm epsilon, >= 0 */
+  float q_out_scale;            /* q outputs are multiplied by this before rounding; 0 means 1 */
 } ha_prologue_desc;
 
 /* HA_ABI_VERSION of the built library. */
@@ -115,6 +119,10 @@ const char* ha_last_error(void);
  * p in [0, n_pos), i in [0, head_dim/2), computed in double and rounded to float.
  * Host-only; theta > 1, head_dim in {64, 128}, n_pos >= 1. */
 ha_status ha_rope_table_fill(double theta, int32_t head_dim, int32_t n_pos, float* host_out);
+
+/* The factor scale * log2(e) that a prescaled q carries (see ha_attn_desc.q_prescaled).
+ * Returns 0 for an invalid descriptor. */
+float ha_q_prescale(const ha_attn_desc* desc);
 
 /* Tile grid used by the attention kernel for this descriptor: block_q query tokens by
  * block_k keys, n_q_blocks x n_k_blocks tiles from index 0 (last row/column ragged). */
@@ -144,16 +152,19 @@ ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
  * when pro is not NULL. */
 size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro);
 
-/* Attention on prepared inputs: q and k already normalised and rotated, row_limit and
- * ranges from ha_classify_tiles for the same descriptor (so the tile plan can be reused
- * across layers and denoising steps). out = softmax(scale * q k^T, masked) v per query
- * head, fp32 accumulation, P rounded to the input dtype for the second product. */
+/* Attention on prepared inputs: q and k already normalised and rotated (q optionally
+ * prescaled, see ha_attn_desc.q_prescaled), row_limit and ranges from ha_classify_tiles
+ * for the same descriptor (so the tile plan can be reused across layers and denoising
+ * steps). out = softmax(scale * q k^T, masked) v per query head, fp32 accumulation, P
+ * rounded to the input dtype for the second product. */
 ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const void* k,
                               const void* v, const int32_t* row_limit, const int32_t* ranges,
                               void* out, void* stream);
 
 /* The whole path: classifier, prologue (skipped when pro is NULL: q, k are then used as
- * given), attention. workspace: DEVICE, 256-byte aligned, >= ha_attn_workspace_bytes. */
+ * given), attention. With a prologue, the q it writes to the workspace is prescaled (its
+ * q_out_scale is ignored) and desc->q_prescaled is ignored. workspace: DEVICE, 256-byte
+ * aligned, >= ha_attn_workspace_bytes. */
 ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
                       const void* k, const void* v, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);

@@ -25,7 +25,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = U.load_library()
     names = declared_functions()
-    assert len(names) == 9 and sorted(B.EXPORTS) == names
+    assert len(names) == 10 and sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
     assert U.ha_abi_version() == 1
@@ -58,6 +58,7 @@ BAD_DESCS = [
      "exceeds"),
     (dict(batch=-1), B.HA_ERR_INVALID_ARG, ">= 0"),
     (dict(n_kv_heads=0), B.HA_ERR_INVALID_ARG, "head counts"),
+    (dict(q_prescaled=2), B.HA_ERR_INVALID_ARG, "q_prescaled"),
 ]
 
 
@@ -109,6 +110,8 @@ BAD_PROLOGUES = [
      B.HA_ERR_INVALID_ARG, "eps"),
     (dict(rope_kind="none", q_norm_weight=FAKE + 1, k_norm_weight=FAKE), B.HA_ERR_ALIGNMENT,
      "aligned"),
+    (dict(rope_kind="none", q_out_scale=-1.0), B.HA_ERR_INVALID_ARG, "q_out_scale"),
+    (dict(rope_kind="none", q_out_scale=float("inf")), B.HA_ERR_INVALID_ARG, "q_out_scale"),
 ]
 
 
@@ -145,6 +148,13 @@ def test_error_text_cleared_by_success():
     assert "head_dim" in U.ha_last_error()
     U.ha_tile_shape(desc())
     assert U.ha_last_error() == ""
+
+
+def test_q_prescale():
+    d = desc()
+    assert abs(U.ha_q_prescale(d) - np.log2(np.e) / 8.0) < 1e-7
+    assert abs(U.ha_q_prescale(desc(scale=0.5)) - 0.5 * np.log2(np.e)) < 1e-7
+    assert U.ha_q_prescale(desc(head_dim=96)) == 0.0
 
 
 def test_tile_shape():

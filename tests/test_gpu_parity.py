@@ -49,6 +49,9 @@ SMALL = {
     "d64_bf16": small([W.Segment(C, 45), W.Segment(G, 81, (9, 9)), W.Segment(C, 3)], d=64,
                       rope="mrope"),
     "one_token": small([W.Segment(C, 1)], batch=3),
+    # rows 0-2 see keys of one lane half only, in a query block that spans several key
+    # tiles (the full rows after them): the row state must stay whole across lane pairs
+    "causal_rows_in_long_block": small([W.Segment(C, 3), W.Segment(F, 130)], hq=4, hkv=1),
     "all_causal": small([W.Segment(C, 300)], rope="1d"),
     "all_full": small([W.Segment(F, 200)], rope="2d", theta=1e4),
     "f32_mixed": small([W.Segment(C, 20), W.Segment(F, 36, (6, 6)), W.Segment(G, 25, (5, 5))],
@@ -228,23 +231,76 @@ def test_future_tokens_do_not_leak():
     assert not torch.equal(b0[0, 97:120], p0[0, 97:120])  # image rows see their whole segment
 
 
-def test_deterministic_and_fwd_equals_planned():
-    w = SMALL["edit_small"]
-    x = W.generate(w)
-    a, dev = run_fwd(x)
-    b, _ = run_fwd(x, dev)
-    assert torch.equal(a, b)
-    desc, pro = desc_for(w), prologue_for(w, dev)
+def planned(x, dev, prescaled):
+    """classifier + prologue + ha_attn_fwd_planned, q prescaled by the prologue or not."""
+    w = x.workload
+    desc = desc_for(w, x.segments)
+    desc.c.q_prescaled = int(prescaled)
+    pro = prologue_for(w, dev)
     bq, bk, nq, nk = B.ha_tile_shape(desc)
     ranges = torch.empty((w.batch, nq, 2), dtype=torch.int32, device="cuda")
     lim = torch.empty((w.batch, w.seq_len), dtype=torch.int32, device="cuda")
     B.ha_classify_tiles(desc, None, ranges, lim)
-    qr, kr = torch.empty_like(dev["q"]), torch.empty_like(dev["k"])
-    B.ha_qk_prologue(desc, pro, dev["q"], dev["k"], qr, kr)
+    qr, kr = dev["q"], dev["k"]
+    if pro is not None or prescaled:
+        pro = pro or B.PrologueDesc("none")
+        pro.c.q_out_scale = B.ha_q_prescale(desc) if prescaled else 0.0
+        qr, kr = torch.empty_like(dev["q"]), torch.empty_like(dev["k"])
+        B.ha_qk_prologue(desc, pro, dev["q"], dev["k"], qr, kr)
     out = torch.empty_like(dev["q"])
     B.ha_attn_fwd_planned(desc, qr, kr, dev["v"], lim, ranges, out)
     torch.cuda.synchronize()
-    assert torch.equal(out, a)
+    return out
+
+
+@pytest.mark.parametrize("name", ["edit_small", "f32_mixed"])
+def test_deterministic_and_fwd_equals_planned(name):
+    w = SMALL[name]
+    x = W.generate(w)
+    a, dev = run_fwd(x)
+    b, _ = run_fwd(x, dev)
+    assert torch.equal(a, b)
+    # ha_attn_fwd writes a prescaled q to its workspace: the same as the planned path
+    assert torch.equal(planned(x, dev, True), a)
+    # plain q through the planned path: a different kernel variant, same result
+    compare(f64(planned(x, dev, False)), oracle.hot_path(x), w.dtype, name + " planned plain q")
+
+
+@pytest.mark.parametrize("name", ["hd_small", "f32_mixed"])
+def test_prologue_q_out_scale(name):
+    w = SMALL[name]
+    x = W.generate(w)
+    dev = to_device(x)
+    desc, pro = desc_for(w), prologue_for(w, dev)
+    pro.c.q_out_scale = 0.37
+    qo, ko = torch.empty_like(dev["q"]), torch.empty_like(dev["k"])
+    B.ha_qk_prologue(desc, pro, dev["q"], dev["k"], qo, ko)
+    torch.cuda.synchronize()
+    q_ref, k_ref = oracle.prologue(x)
+    tol = (lambda want: 2.0 ** -7 * np.abs(want) + 1e-6) if w.dtype == "bf16" else (
+        lambda want: 1e-5 * np.abs(want).max())
+    assert (np.abs(f64(qo) - 0.37 * q_ref) <= tol(0.37 * q_ref)).all()
+    assert (np.abs(f64(ko) - k_ref) <= tol(k_ref)).all()
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+@pytest.mark.parametrize("prescaled", [False, True])
+def test_extreme_logits_take_the_rescale_path(sign, prescaled):
+    """Scores far above (sign +1, about +33 in log2 units) or far below (sign -1, about
+    -165, where every exp2 underflows even as a denormal) the initial reference force the
+    re-reference path. q and k share a strong common direction e_0, which shifts each row by
+    a constant, so the softmax itself stays well conditioned. (A prescaled q is rounded
+    after the scale, so its error grows with the common component; 36 keeps it small.)"""
+    w = small([W.Segment(C, 40), W.Segment(F, 100), W.Segment(G, 61)], rope="none", norm=False,
+              hq=8, hkv=2)
+    x = W.generate(w)
+    alpha = 16.0 if sign > 0 else 36.0
+    x.q[..., 0] += sign * alpha
+    x.k[..., 0] += alpha
+    refresh_bits(x)
+    dev = to_device(x)
+    got = f64(planned(x, dev, prescaled))
+    compare(got, oracle.hot_path(x), "bf16", f"extreme logits sign {sign} prescaled {prescaled}")
 
 
 def test_per_batch_layouts_differ():

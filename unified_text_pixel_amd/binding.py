@@ -25,8 +25,8 @@ HA_TILE_SKIP, HA_TILE_FULL, HA_TILE_PARTIAL = 0, 1, 2
 ROPE_KINDS = {"none": HA_ROPE_NONE, "1d": HA_ROPE_1D, "2d": HA_ROPE_2D, "mrope": HA_ROPE_MROPE}
 
 # Every function include/ha_attn.h declares.
-EXPORTS = ("ha_abi_version", "ha_last_error", "ha_rope_table_fill", "ha_tile_shape",
-           "ha_classify_tiles", "ha_qk_prologue", "ha_attn_workspace_bytes",
+EXPORTS = ("ha_abi_version", "ha_last_error", "ha_rope_table_fill", "ha_q_prescale",
+           "ha_tile_shape", "ha_classify_tiles", "ha_qk_prologue", "ha_attn_workspace_bytes",
            "ha_attn_fwd_planned", "ha_attn_fwd")
 
 
@@ -45,14 +45,15 @@ class ha_attn_desc(ctypes.Structure):
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("segments", ctypes.POINTER(ha_segment)), ("n_segments", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("q_prescaled", ctypes.c_int32)]
 
 
 class ha_prologue_desc(ctypes.Structure):
     _fields_ = [("rope_kind", ctypes.c_int32), ("mrope_sections", ctypes.c_int32 * 3),
                 ("positions", ctypes.c_void_p), ("cos_sin", ctypes.c_void_p),
                 ("n_pos", ctypes.c_int32), ("q_norm_weight", ctypes.c_void_p),
-                ("k_norm_weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+                ("k_norm_weight", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("q_out_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -74,6 +75,7 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
         "ha_abi_version": ([], ctypes.c_int),
         "ha_last_error": ([], ctypes.c_char_p),
         "ha_rope_table_fill": ([ctypes.c_double, I32, I32, P], ctypes.c_int),
+        "ha_q_prescale": ([D], ctypes.c_float),
         "ha_tile_shape": ([D, P, P, P, P], ctypes.c_int),
         "ha_classify_tiles": ([D, P, P, P, P], ctypes.c_int),
         "ha_qk_prologue": ([D, PD, P, P, P, P, P], ctypes.c_int),
@@ -115,7 +117,7 @@ class AttnDesc:
     """Owns an ha_attn_desc and the host segment array it points to."""
 
     def __init__(self, batch, seq_len, n_q_heads, n_kv_heads, head_dim, dtype, segments,
-                 scale: float = 0.0):
+                 scale: float = 0.0, q_prescaled: int = 0):
         seg = np.asarray(segments, dtype=np.int32)
         if batch > 0 and seq_len > 0:
             seg = np.ascontiguousarray(seg.reshape(batch, -1, 3))
@@ -129,17 +131,17 @@ class AttnDesc:
         dt = {"bf16": HA_DTYPE_BF16, "f32": HA_DTYPE_F32}.get(dtype, dtype)
         self.c = ha_attn_desc(batch, seq_len, n_q_heads, n_kv_heads, head_dim, dt,
                               ctypes.cast(self._seg, ctypes.POINTER(ha_segment)), n_seg,
-                              float(scale))
+                              float(scale), int(q_prescaled))
 
 
 class PrologueDesc:
     def __init__(self, rope_kind, positions=None, cos_sin=None, n_pos=0, q_norm_weight=None,
-                 k_norm_weight=None, eps=1e-6, mrope_sections=(0, 0, 0)):
+                 k_norm_weight=None, eps=1e-6, mrope_sections=(0, 0, 0), q_out_scale=0.0):
         kind = ROPE_KINDS.get(rope_kind, rope_kind)
         self._keep = (positions, cos_sin, q_norm_weight, k_norm_weight)
         self.c = ha_prologue_desc(kind, (ctypes.c_int32 * 3)(*mrope_sections), _ptr(positions),
                                   _ptr(cos_sin), int(n_pos), _ptr(q_norm_weight),
-                                  _ptr(k_norm_weight), float(eps))
+                                  _ptr(k_norm_weight), float(eps), float(q_out_scale))
 
 
 def _d(desc):
@@ -166,6 +168,11 @@ def ha_rope_table_fill(theta: float, head_dim: int, n_pos: int) -> np.ndarray:
     _check(lib.ha_rope_table_fill(float(theta), head_dim, n_pos,
                                   out.ctypes.data_as(ctypes.c_void_p) if out.size else None))
     return out
+
+
+def ha_q_prescale(desc: AttnDesc) -> float:
+    """scale * log2(e): the factor a prescaled q carries (0.0 for an invalid descriptor)."""
+    return float(load_library().ha_q_prescale(_d(desc)))
 
 
 def ha_tile_shape(desc: AttnDesc):

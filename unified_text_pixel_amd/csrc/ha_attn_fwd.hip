@@ -35,6 +35,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kHi = 1048576.0f;             // 2^20: largest tile row sum taken as is
+constexpr float kLo = 8.673617379884035e-19f; // 2^-60: smallest running row sum taken as is
+constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int BK = kBlockK;
 
@@ -72,6 +77,31 @@ __device__ inline float wave_pair_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// P = exp2(S) (S in log2 units when q is prescaled, else scaled by c here) for one
+// 64-key tile, rounded to bf16 in the B-operand order of the second product; returns the
+// lane's sum of the rounded values (two keys per v_dot2, two chains).
+template <bool PRE>
+__device__ inline float exp_tile(const f32x16 (&s)[2], float c, bf16x8 (&pf)[4]) {
+#pragma unroll
+  for (int KS = 0; KS < 4; ++KS)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = s[KS >> 1][(KS & 1) * 8 + e];
+      pf[KS][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(PRE ? x : x * c));
+    }
+  float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+  for (int KS = 0; KS < 4; ++KS)
+#pragma unroll
+    for (int t = 0; t < 4; t += 2) {
+      const bf16x2 p0 = {pf[KS][2 * t], pf[KS][2 * t + 1]};
+      const bf16x2 p1 = {pf[KS][2 * t + 2], pf[KS][2 * t + 3]};
+      t0 = __builtin_amdgcn_fdot2_f32_bf16(p0, kOnes, t0, false);
+      t1 = __builtin_amdgcn_fdot2_f32_bf16(p1, kOnes, t1, false);
+    }
+  return t0 + t1;
+}
+
 // Position of key kk (0..BK-1) inside a staged V^T row: chunks of 4 keys within each
 // 16-key group are stored in the order [0, 2, 1, 3].
 __device__ inline int vt_pos(int kk) {
@@ -85,30 +115,65 @@ struct Stage {
   using C = Cfg<D, G, F32>;
   bf16x8 kr[C::KCH];
   bf16x8 vr[C::VT][4];
+  const __bf16* kbase;  // k and v of this (batch, KV head) at key 0 (uniform)
+  const __bf16* vbase;
+  int64_t tile_stride;  // elements between consecutive key tiles
+  int rows_left0;       // S
+  int koff[C::KCH];     // per-thread element offsets inside a tile
+  int voff[C::VT];
 
-  __device__ inline void load(const AttnArgs& a, int b, int g, int kb) {
+  __device__ inline void init(const AttnArgs& a, int b, int g) {
+    const int rs = a.Hkv * D;  // elements between consecutive keys
+    kbase = static_cast<const __bf16*>(a.k) + ((int64_t)b * a.S * a.Hkv + g) * D;
+    vbase = static_cast<const __bf16*>(a.v) + ((int64_t)b * a.S * a.Hkv + g) * D;
+    tile_stride = (int64_t)BK * rs;
+    rows_left0 = a.S;
     const int tid = threadIdx.x;
-    const __bf16* kp = static_cast<const __bf16*>(a.k);
-    const __bf16* vp = static_cast<const __bf16*>(a.v);
-    const bf16x8 zero = {};
+#pragma unroll
     for (int j = 0; j < C::KCH; ++j) {
       const int c = tid + j * C::NT;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      const int gk = kb * BK + key;
-      kr[j] = (c < BK * D / 8 && gk < a.S)
-                  ? *reinterpret_cast<const bf16x8*>(kp + (((int64_t)b * a.S + gk) * a.Hkv + g) * D + 8 * dc)
-                  : zero;
+      koff[j] = (c / (D / 8)) * rs + 8 * (c % (D / 8));
     }
+#pragma unroll
     for (int j = 0; j < C::VT; ++j) {
       const int t = tid + j * C::NT;
-      const int kg = t % (BK / 4), dc = t / (BK / 4);
+      voff[j] = 4 * (t % (BK / 4)) * rs + 8 * (t / (BK / 4));
+    }
+  }
+
+  // Global -> registers for key tile kb. Only a tile that runs past the sequence end
+  // (RAGGED) checks rows; its missing rows are zero.
+  template <bool RAGGED>
+  __device__ inline void load(int kb) {
+    const int tid = threadIdx.x;
+    const __bf16* kt = kbase + kb * tile_stride;
+    const __bf16* vt = vbase + kb * tile_stride;
+    const int left = rows_left0 - kb * BK;  // keys of this tile inside the sequence
+    const int rs = (int)(tile_stride / BK);
+    const bf16x8 zero = {};
+#pragma unroll
+    for (int j = 0; j < C::KCH; ++j) {
+      const int c = tid + j * C::NT;
+      const bool ok = (C::KCH * C::NT == BK * D / 8 || c < BK * D / 8) && (!RAGGED || c / (D / 8) < left);
+      kr[j] = ok ? *reinterpret_cast<const bf16x8*>(kt + koff[j]) : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < C::VT; ++j) {
+      const int t = tid + j * C::NT;
+#pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int gk = kb * BK + 4 * kg + u;
-        vr[j][u] = (t < C::VTASKS && gk < a.S)
-                       ? *reinterpret_cast<const bf16x8*>(vp + (((int64_t)b * a.S + gk) * a.Hkv + g) * D + 8 * dc)
-                       : zero;
+        const bool ok = (C::VT * C::NT == C::VTASKS || t < C::VTASKS) &&
+                        (!RAGGED || 4 * (t % (BK / 4)) + u < left);
+        vr[j][u] = ok ? *reinterpret_cast<const bf16x8*>(vt + voff[j] + u * rs) : zero;
       }
     }
+  }
+
+  __device__ inline void load_tile(int kb) {
+    if ((kb + 1) * BK <= rows_left0)
+      load<false>(kb);
+    else
+      load<true>(kb);
   }
 
   __device__ inline void commit(__bf16* buf) {
@@ -117,14 +182,14 @@ struct Stage {
     __bf16* vt = buf + C::K_ELEMS;
     for (int j = 0; j < C::KCH; ++j) {
       const int c = tid + j * C::NT;
-      if (c < BK * D / 8) {
+      if (C::KCH * C::NT == BK * D / 8 || c < BK * D / 8) {
         const int key = c / (D / 8), dc = c % (D / 8);
         *reinterpret_cast<bf16x8*>(ks + key * C::KP + 8 * dc) = kr[j];
       }
     }
     for (int j = 0; j < C::VT; ++j) {
       const int t = tid + j * C::NT;
-      if (t < C::VTASKS) {
+      if (C::VT * C::NT == C::VTASKS || t < C::VTASKS) {
         const int kg = t % (BK / 4), dc = t / (BK / 4);
         const int pos = vt_pos(4 * kg);
         // 4 keys x 8 dims -> 8 rows of 4 consecutive keys, on 32-bit words (two bf16 each)
@@ -142,7 +207,7 @@ struct Stage {
   }
 };
 
-template <int D, int G, bool F32>
+template <int D, int G, bool F32, bool PRE>
 __global__ __launch_bounds__((Cfg<D, G, F32>::NT), 2) void attn_kernel(AttnArgs a) {
   using C = Cfg<D, G, F32>;
   using T = typename C::T;
@@ -182,16 +247,23 @@ __global__ __launch_bounds__((Cfg<D, G, F32>::NT), 2) void attn_kernel(AttnArgs 
 
   f32x16 o[D / 32];
   for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float lfinal;
 
   if constexpr (!F32) {
+    // Softmax state of this lane's row, in log2 units: reference m (not necessarily the
+    // running max) and l = sum of exp2(score - m) over the row's keys seen so far. negm holds -m in the
+    // units of the S accumulator (log2 units when q is prescaled, raw otherwise) and is
+    // the C operand of each tile's first MFMA, so the subtraction costs nothing.
+    float m = 0.f, l = 0.f;
+    f32x16 negm = f32x16{};
     const __bf16* qp = static_cast<const __bf16*>(a.q);
     bf16x8 qf[D / 16];
     for (int ks = 0; ks < D / 16; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + qrow + 16 * ks + 8 * hi);
 
     Stage<D, G, F32> st;
-    st.load(a, b, g, 0);
+    st.init(a, b, g);
+    st.load_tile(0);
     st.commit(lds);
     __syncthreads();
 
@@ -199,60 +271,95 @@ __global__ __launch_bounds__((Cfg<D, G, F32>::NT), 2) void attn_kernel(AttnArgs 
       const __bf16* ks_lds = lds + (kb & 1) * C::BUF;
       const __bf16* vt_lds = ks_lds + C::K_ELEMS;
       const bool more = kb + 1 < kend;
-      if (more) st.load(a, b, g, kb + 1);
+      if (more) st.load_tile(kb + 1);
 
+      // S^T - m for the two 32-key halves, interleaved so the chains overlap
       f32x16 s[2];
-      for (int kt = 0; kt < 2; ++kt) {
-        s[kt] = f32x16{};
-        const __bf16* krow = ks_lds + (32 * kt + (lane & 31)) * C::KP + 8 * hi;
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[kt], 0, 0, 0);
+      {
+        const __bf16* krow = ks_lds + (lane & 31) * C::KP + 8 * hi;
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow + 32 * C::KP);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[0], negm, 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[0], negm, 0, 0, 0);
+#pragma unroll
+        for (int kk = 1; kk < D / 16; ++kk) {
+          const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+          const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(krow + 32 * C::KP + 16 * kk);
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, qf[kk], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, qf[kk], s[1], 0, 0, 0);
         }
       }
 
       if (kb >= kfull || (kb + 1) * BK > S) {
+#pragma unroll
         for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kb * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= lim) s[kt][r] = -INFINITY;
+            s[kt][r] = key >= lim ? -INFINITY : s[kt][r];
           }
       }
 
-      float mx = -INFINITY;
-      for (int kt = 0; kt < 2; ++kt)
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      mx = wave_pair_max(mx);
-      const float mnew = fmaxf(m, mx);
-      const float mc = (mnew == -INFINITY) ? 0.f : mnew * c;
-      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m * c - mc);
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      // Fast path: P = exp2(S - m) as is. It is taken unless some row's tile sum leaves
+      // [kLo, kHi] (or is not finite), in which case those rows are re-referenced first;
+      // either way numerator and denominator share the reference, so the result is the
+      // softmax up to rounding.
+      // A row lives in two lanes (one per 16-key half of every 32 keys) and their O^T
+      // registers hold different output dims accumulated from both halves' P, so the
+      // row's state (l, m, the re-reference decision) is kept whole in both lanes: the
+      // tile sum is reduced over the pair first.
+      bf16x8 pf[4];
+      float ts = wave_pair_sum(exp_tile<PRE>(s, c, pf));
+      const bool bad = !(ts <= kHi) || !(l + ts >= kLo);
+      if (__builtin_amdgcn_ballot_w64(bad)) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        mx = wave_pair_max(mx);
+        if (!PRE) mx *= c;
+        // new reference (relative to m): the larger of the tile max and log2(l), so both
+        // the old sum and the new tile end up <= 1 and at least one of them near 1
+        float sh = fmaxf(mx, __builtin_amdgcn_logf(l));
+        sh = (bad && sh > -INFINITY) ? sh : 0.f;
+        m += sh;
+        // alpha <= 1/l for l > 0 (sh >= log2 l), and l >= 2^-60 outside the first tile, so
+        // it cannot overflow; with l = 0 nothing has been accumulated (O = 0) and it is 0
+        const float alpha = l == 0.f ? 0.f : __builtin_amdgcn_exp2f(-sh);
+#pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
-      }
-      l *= alpha;
-      m = mnew;
-      for (int kt = 0; kt < 2; ++kt)
+        l *= alpha;
+        const float shs = PRE ? sh : sh / c;  // in accumulator units
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[kt][r] * c - mc);
-          s[kt][r] = p;
-          l += p;
+          negm[r] -= shs;
+          s[0][r] -= shs;
+          s[1][r] -= shs;
         }
+        ts = wave_pair_sum(exp_tile<PRE>(s, c, pf));
+      }
+      l += ts;
 
+      // O^T += V^T P^T
+#pragma unroll
       for (int KS = 0; KS < BK / 16; ++KS) {
-        const int kt = KS >> 1, base = (KS & 1) * 8;
-        bf16x8 pf;
-        for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(s[kt][base + e]);
         const __bf16* vrow = vt_lds + (lane & 31) * C::VP + 16 * KS + 8 * hi;
+#pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
           const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * C::VP);
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[mt], 0, 0, 0);
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[KS], o[mt], 0, 0, 0);
         }
       }
 
       if (more) st.commit(lds + ((kb + 1) & 1) * C::BUF);
       __syncthreads();
     }
+    lfinal = l;
   } else {
+    // fp32 inputs: plain online softmax with the running max, fp32 P.
+    float m = -INFINITY, l = 0.f;
+    const float cs = PRE ? 1.f : c;
     const float* qp = static_cast<const float*>(a.q);
     const float* kp = static_cast<const float*>(a.k);
     const float* vp = static_cast<const float*>(a.v);
@@ -291,14 +398,14 @@ __global__ __launch_bounds__((Cfg<D, G, F32>::NT), 2) void attn_kernel(AttnArgs 
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
       mx = wave_pair_max(mx);
       const float mnew = fmaxf(m, mx);
-      const float mc = (mnew == -INFINITY) ? 0.f : mnew * c;
-      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m * c - mc);
+      const float mc = (mnew == -INFINITY) ? 0.f : mnew * cs;
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m * cs - mc);
       for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
       l *= alpha;
       m = mnew;
       for (int kt = 0; kt < 2; ++kt)
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[kt][r] * c - mc);
+          const float p = exp2f(s[kt][r] * cs - mc);
           s[kt][r] = p;
           l += p;
         }
@@ -312,9 +419,10 @@ __global__ __launch_bounds__((Cfg<D, G, F32>::NT), 2) void attn_kernel(AttnArgs 
             o[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * mt], s[kt][t], o[mt], 0, 0, 0);
         }
     }
+    lfinal = wave_pair_sum(l);  // per-lane partial sums over the two key halves
   }
 
-  const float inv = 1.f / wave_pair_sum(l);
+  const float inv = 1.f / lfinal;
   if (row_ok) {
     const int64_t orow = (((int64_t)b * S + i) * a.Hq + h) * D;
     for (int mt = 0; mt < D / 32; ++mt)
@@ -337,7 +445,10 @@ template <int D, int G, bool F32>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D, G, F32>;
   const int64_t items = (int64_t)a.B * a.Hkv * a.nq;
-  hipLaunchKernelGGL((attn_kernel<D, G, F32>), dim3((unsigned)items), dim3(C::NT), 0, stream, a);
+  if (a.q_prescaled)
+    hipLaunchKernelGGL((attn_kernel<D, G, F32, true>), dim3((unsigned)items), dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, G, F32, false>), dim3((unsigned)items), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -81,6 +81,8 @@ ha_status check_desc(const ha_attn_desc* d) {
     return fail(HA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
   if (!std::isfinite(d->scale) || d->scale < 0.f)
     return fail(HA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (d->q_prescaled != 0 && d->q_prescaled != 1)
+    return fail(HA_ERR_INVALID_ARG, "q_prescaled must be 0 or 1");
   if ((int64_t)d->n_q_heads * d->head_dim * (int64_t)d->seq_len * (d->batch ? d->batch : 1) >
       (int64_t(1) << 40))
     return fail(HA_ERR_UNSUPPORTED, "tensor too large");
@@ -141,6 +143,8 @@ ha_status check_prologue(const ha_attn_desc* d, const ha_prologue_desc* p) {
       return fail(HA_ERR_ALIGNMENT, "norm weights must be 4-byte aligned");
     if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(HA_ERR_INVALID_ARG, "eps must be finite and >= 0");
   }
+  if (!std::isfinite(p->q_out_scale) || p->q_out_scale < 0.f)
+    return fail(HA_ERR_INVALID_ARG, "q_out_scale must be finite and >= 0");
   if ((d->n_q_heads + d->n_kv_heads) * (d->head_dim / 16) > 1024)
     return fail(HA_ERR_UNSUPPORTED, "prologue: (n_q_heads + n_kv_heads) * head_dim / 16 must be <= 1024");
   return HA_OK;
@@ -205,8 +209,14 @@ void axis_table(const ha_prologue_desc* p, int head_dim, uint8_t* axis) {
   }
 }
 
+double softmax_scale(const ha_attn_desc* d) {
+  return d->scale > 0.f ? (double)d->scale : 1.0 / std::sqrt((double)d->head_dim);
+}
+
+float q_prescale(const ha_attn_desc* d) { return (float)(softmax_scale(d) * 1.4426950408889634074); }
+
 ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const void* q_in, const void* k_in,
-                       void* q_out, void* k_out, hipStream_t stream) {
+                       void* q_out, void* k_out, float q_scale, hipStream_t stream) {
   ha::PrologueArgs a{};
   a.q_in = q_in;
   a.k_in = k_in;
@@ -225,13 +235,14 @@ ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const v
   a.n_axes = n_axes_of(p->rope_kind);
   a.n_pos = p->n_pos;
   a.eps = p->eps;
+  a.q_scale = q_scale;
   a.f32 = d->dtype == HA_DTYPE_F32;
   axis_table(p, d->head_dim, a.axis);
   return check_launch(ha::launch_prologue(a, stream), stream, "prologue");
 }
 
 ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const void* v, const int32_t* row_limit,
-                   const int32_t* ranges, void* out, hipStream_t stream) {
+                   const int32_t* ranges, void* out, bool prescaled, hipStream_t stream) {
   ha::AttnArgs a{};
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
@@ -247,8 +258,8 @@ ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const vo
   a.Hkv = d->n_kv_heads;
   a.D = d->head_dim;
   a.nq = nq;
-  const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / std::sqrt((double)d->head_dim);
-  a.scale_log2e = (float)(scale * 1.4426950408889634074);
+  a.scale_log2e = q_prescale(d);
+  a.q_prescaled = prescaled;
   a.f32 = d->dtype == HA_DTYPE_F32;
   return check_launch(ha::launch_attn(a, stream), stream, "attention");
 }
@@ -302,6 +313,12 @@ ha_status ha_rope_table_fill(double theta, int32_t head_dim, int32_t n_pos, floa
   return ok();
 }
 
+float ha_q_prescale(const ha_attn_desc* desc) {
+  if (check_desc(desc) != HA_OK) return 0.f;
+  g_last_error.clear();
+  return q_prescale(desc);
+}
+
 ha_status ha_tile_shape(const ha_attn_desc* desc, int32_t* block_q, int32_t* block_k, int32_t* n_q_blocks,
                         int32_t* n_k_blocks) {
   ha_status st = check_desc(desc);
@@ -337,7 +354,8 @@ ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro, 
   if ((st = check_tensor(q_in, "q_in")) != HA_OK || (st = check_tensor(k_in, "k_in")) != HA_OK ||
       (st = check_tensor(q_out, "q_out")) != HA_OK || (st = check_tensor(k_out, "k_out")) != HA_OK)
     return st;
-  st = run_prologue(desc, pro, q_in, k_in, q_out, k_out, static_cast<hipStream_t>(stream));
+  st = run_prologue(desc, pro, q_in, k_in, q_out, k_out, pro->q_out_scale > 0.f ? pro->q_out_scale : 1.f,
+                    static_cast<hipStream_t>(stream));
   return st == HA_OK ? ok() : st;
 }
 
@@ -357,7 +375,7 @@ ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const voi
   if (!row_limit || !ranges) return fail(HA_ERR_INVALID_ARG, "row_limit and ranges are required");
   if (!aligned(row_limit, 4) || !aligned(ranges, 4))
     return fail(HA_ERR_ALIGNMENT, "row_limit and ranges must be 4-byte aligned");
-  st = run_attn(desc, q, k, v, row_limit, ranges, out, static_cast<hipStream_t>(stream));
+  st = run_attn(desc, q, k, v, row_limit, ranges, out, desc->q_prescaled == 1, static_cast<hipStream_t>(stream));
   return st == HA_OK ? ok() : st;
 }
 
@@ -385,11 +403,11 @@ ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   if (pro) {
     void* qr = ws + w.q_rot;
     void* kr = ws + w.k_rot;
-    if ((st = run_prologue(desc, pro, q, k, qr, kr, s)) != HA_OK) return st;
+    if ((st = run_prologue(desc, pro, q, k, qr, kr, q_prescale(desc), s)) != HA_OK) return st;
     qa = qr;
     ka = kr;
   }
-  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, s);
+  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, pro != nullptr, s);
   return st == HA_OK ? ok() : st;
 }
 

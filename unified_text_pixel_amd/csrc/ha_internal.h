@@ -40,6 +40,7 @@ struct PrologueArgs {
   int32_t B, S, Hq, Hkv, D, n_axes, n_pos;
   int32_t rotate;  // 0: no rotary embedding
   float eps;
+  float q_scale;   // q outputs are multiplied by this before rounding
   int32_t f32;     // 1: fp32 tensors, 0: bf16
   uint8_t axis[64];  // rotary axis of pair i
 };
@@ -58,6 +59,7 @@ struct AttnArgs {
   const int32_t* ranges;     // [B][nq][2]
   int32_t B, S, Hq, Hkv, D, nq;
   float scale_log2e;         // softmax scale * log2(e)
+  int32_t q_prescaled;       // 1: q already carries scale_log2e
   int32_t f32;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);

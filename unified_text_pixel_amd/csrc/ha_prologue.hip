@@ -92,6 +92,12 @@ __global__ __launch_bounds__(1024) void prologue_kernel(PrologueArgs a) {
       x2[e] = y2;
     }
   }
+  if (isq && a.q_scale != 1.f) {
+    for (int e = 0; e < 8; ++e) {
+      x1[e] *= a.q_scale;
+      x2[e] *= a.q_scale;
+    }
+  }
   store8<F32>(out, base + 8 * c, x1);
   store8<F32>(out, base + HALF + 8 * c, x2);
 }
