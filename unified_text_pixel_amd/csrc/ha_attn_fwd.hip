@@ -29,6 +29,7 @@
 // row's tile sum leaves [2^-60, 2^20] is the row re-referenced (exactly; see below).
 // fp32 inputs use a plain variant (fp32 P, v_mfma_f32_32x32x2_f32, running max).
 #include <array>
+#include <type_traits>
 
 #include "ha_internal.h"
 
@@ -125,11 +126,9 @@ struct Tile {
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int BYTES = BK * D * 2;      // one tile
   static constexpr int NI = BYTES / 1024;       // 1 KB DMA instructions per tile
+  static constexpr int RPI = 1024 / (2 * D);    // rows per DMA instruction
   __device__ static inline int kswz(int row) { return row & (CPR - 1); }
-  __device__ static inline int vswz(int row) {
-    const int r = row & 3;
-    return (r == 0 ? 0 : (r == 1 ? 6 : (r == 2 ? 10 : 12))) & (CPR - 1);
-  }
+  __device__ static inline int vswz(int row) { return (0xCA60 >> (4 * (row & 3))) & (CPR - 1); }
 };
 
 template <int D, int G>
@@ -142,27 +141,58 @@ struct CfgB {
   static_assert(Tile<D>::NI % NW == 0, "DMA instructions must split evenly over waves");
 };
 
-// DMA of one key tile (BK rows of K or V for this batch item and KV head) into a swizzled
-// LDS buffer. Instruction j of wave w covers tile bytes [1024 (w*IPW + j), +1024); lane L
-// writes bytes +16 L, i.e. row rr, physical chunk pc, which holds logical chunk pc ^ swz.
-// Rows past the sequence end read its last row instead (never used: masked keys get P = 0
-// and that row is finite).
-template <int D, int G, bool ISV>
-__device__ inline void dma_tile(const __bf16* base, int64_t rs, int key0, int S, char* buf, int wave,
-                                int lane) {
+// DMA of key tiles (BK rows of K or V for one batch item and KV head) into swizzled LDS
+// buffers. DMA instruction ins covers tile bytes [1024 ins, +1024): lane L writes bytes
+// +16 L, i.e. tile row RPI*ins + L/CPR at physical chunk L%CPR, which holds logical chunk
+// (L%CPR) ^ swizzle(row). Since RPI is a multiple of 4 and L/CPR < RPI, that logical
+// chunk is, for V, a per-lane constant and, for K, a per-lane constant XOR a per-
+// instruction constant; the global address is a uniform base plus a per-lane offset.
+// Rows past the sequence end (only in the last tile) read its last row instead: masked
+// keys get P = 0 and that row is finite.
+template <int D, int G>
+struct Dma {
   using TL = Tile<D>;
-#pragma unroll
-  for (int j = 0; j < CfgB<D, G>::IPW; ++j) {
-    const int ins = wave * CfgB<D, G>::IPW + j;
-    const int byte = ins * 1024 + lane * 16;
-    const int rr = byte / (2 * D);
-    const int pc = (byte % (2 * D)) / 16;
-    const int c = pc ^ (ISV ? TL::vswz(rr) : TL::kswz(rr));
-    const int row = min(key0 + rr, S - 1);
-    const __bf16* src = base + row * rs + 8 * c;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + ins * 1024), 16, 0, 0);
+  const char* kbase;  // key 0 of this batch item and KV head (uniform)
+  const char* vbase;
+  int64_t row_bytes;  // bytes between consecutive keys
+  int S, wave, lrow;  // lrow = lane / CPR
+  unsigned koff, kx16, voff, lane16;
+
+  __device__ inline void init(const void* k, const void* v, int b, int g, int S_, int Hkv, int wave_,
+                              int lane) {
+    row_bytes = (int64_t)Hkv * D * 2;
+    kbase = static_cast<const char*>(k) + ((int64_t)b * S_ * Hkv + g) * D * 2;
+    vbase = static_cast<const char*>(v) + ((int64_t)b * S_ * Hkv + g) * D * 2;
+    S = S_;
+    wave = wave_;
+    lrow = lane / TL::CPR;
+    const int pc = lane % TL::CPR;
+    koff = (unsigned)(lrow * row_bytes);
+    kx16 = 16u * (unsigned)(pc ^ lrow);
+    voff = (unsigned)(lrow * row_bytes) + 16u * (unsigned)(pc ^ TL::vswz(lrow));
+    lane16 = 16u * (unsigned)pc;
   }
-}
+
+  // CLAMP: the tile may run past the sequence end (per-lane row clamp)
+  template <bool ISV, bool CLAMP>
+  __device__ inline void tile(int key0, char* buf) const {
+#pragma unroll
+    for (int j = 0; j < CfgB<D, G>::IPW; ++j) {
+      const int ins = wave * CfgB<D, G>::IPW + j;
+      const char* src;
+      if constexpr (!CLAMP) {
+        const char* g = (ISV ? vbase : kbase) + (key0 + TL::RPI * ins) * row_bytes;
+        const unsigned u = 16u * (unsigned)((TL::RPI * ins) & (TL::CPR - 1));
+        src = g + (ISV ? voff : koff + (kx16 ^ u));
+      } else {
+        const int rr = TL::RPI * ins + lrow;
+        const int c = (int)(lane16 / 16u) ^ (ISV ? TL::vswz(rr) : TL::kswz(rr));
+        src = (ISV ? vbase : kbase) + min(key0 + rr, S - 1) * row_bytes + 16 * c;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + ins * 1024), 16, 0, 0);
+    }
+  }
+};
 
 template <int D, int G, bool PRE>
 __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
@@ -174,7 +204,8 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
 
   const Item it = work_item(a);
   const int b = it.b, g = it.g, qb = it.qb;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave % G, tsub = wave / G;
   const int h = g * G + hg;
   const int hi = lane >> 5;
@@ -186,9 +217,8 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   const int kfull = a.ranges[((int64_t)b * a.nq + qb) * 2 + 0];
   const int kend = a.ranges[((int64_t)b * a.nq + qb) * 2 + 1];
   const float c = a.scale_log2e;
-  const int64_t rs = (int64_t)a.Hkv * D;  // elements between consecutive keys
-  const __bf16* kbase = static_cast<const __bf16*>(a.k) + ((int64_t)b * S * a.Hkv + g) * D;
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + ((int64_t)b * S * a.Hkv + g) * D;
+  Dma<D, G> dma;
+  dma.init(a.k, a.v, b, g, S, a.Hkv, wave, lane);
 
   // K-operand reads: row 32kt + (lane & 31), logical chunk 2kk + hi
   const int krow = lane & 31;
@@ -234,52 +264,57 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     return s;
   };
 
-  // prologue: K0, V0, K1 in flight; S_0
-  dma_tile<D, G, false>(kbase, rs, 0, S, kbuf0, wave, lane);
-  dma_tile<D, G, true>(vbase, rs, 0, S, vbuf0, wave, lane);
-  if (kend > 1) dma_tile<D, G, false>(kbase, rs, BK, S, kbuf0 + TL::BYTES, wave, lane);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  f32x16 sc[2];
-  {
-    const auto s0 = qk(kbuf0);
-    sc[0] = s0[0];
-    sc[1] = s0[1];
-  }
+  // Masks tile t of S (keys >= lim) where the tile is partial or runs past the end.
+  auto mask = [&](f32x16 (&sc)[2], int t) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
+        sc[kt][r] = key >= lim ? -INFINITY : sc[kt][r];
+      }
+  };
 
-  for (int t = 0; t < kend; ++t) {
-    // K_{t+1} and V_t have landed; every wave is done with tile t-1's buffers
+  // O^T += V^T P^T for one tile; the A operand of K step KS, dims 32mt.. comes from two
+  // transposing reads (keys +0..3 and +8..11 of the lane's half)
+  auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) {
+#pragma unroll
+    for (int KS = 0; KS < BK / 16; ++KS)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const char* p0 = vb + (16 * KS + vrow) * (2 * D) + (((4 * mt) ^ vx) * 16) + vhalf;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * 2 * D));
+        const bf16x8 vf = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[KS], o[mt], 0, 0, 0);
+      }
+  };
+
+  // One pipeline step for tile t: land K_{t+1} and V_{t-1}, start the DMA of K_{t+2} and
+  // V_t, then S_{t+1} = K_{t+1} Q^T - m, O += V_{t-1} P_{t-1} and P_t = exp2(S_t - m).
+  // FAST steps (tiles t-1 .. t+2 present, tiles t .. t+2 full and inside the sequence)
+  // have no branch before the re-reference check, so those two MFMA chains and the
+  // exponentials are free to interleave.
+  auto step = [&](auto fast_tag, int t, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pfp)[4],
+                  bf16x8 (&pf)[4]) {
+    constexpr bool FAST = decltype(fast_tag)::value;
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 2 < kend)
-      dma_tile<D, G, false>(kbase, rs, (t + 2) * BK, S, kbuf0 + (t & 1) * TL::BYTES, wave, lane);
-    if (t + 1 < kend)
-      dma_tile<D, G, true>(vbase, rs, (t + 1) * BK, S, vbuf0 + ((t + 1) & 1) * TL::BYTES, wave, lane);
-
-    // S_{t+1}: independent of the softmax below, so the two can overlap
-    f32x16 sn[2] = {f32x16{}, f32x16{}};
-    if (t + 1 < kend) {
+    if (FAST || t + 2 < kend) dma.template tile<false, !FAST>((t + 2) * BK, kbuf0 + (t & 1) * TL::BYTES);
+    dma.template tile<true, !FAST>(t * BK, vbuf0 + (t & 1) * TL::BYTES);
+    if (FAST || t + 1 < kend) {
       const auto s1 = qk(kbuf0 + ((t + 1) & 1) * TL::BYTES);
       sn[0] = s1[0];
       sn[1] = s1[1];
     }
-
-    if (t >= kfull || (t + 1) * BK > S) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-          sc[kt][r] = key >= lim ? -INFINITY : sc[kt][r];
-        }
-    }
+    if (FAST || t >= 1) pv(vbuf0 + ((t - 1) & 1) * TL::BYTES, pfp);
+    if (!FAST && (t >= kfull || (t + 1) * BK > S)) mask(sc, t);
 
     // Fast path: P = exp2(S - m) as is. It is taken unless some row's tile sum leaves
     // [kLo, kHi] (or is not finite); those rows are first re-referenced to the larger of
     // the tile max and log2(l), so both the old sum and the new tile end up <= 1 with one
-    // of them near 1. Numerator and denominator share the reference either way, so the
-    // result is the softmax up to rounding.
-    bf16x8 pf[4];
+    // of them near 1. Numerator and denominator share the reference either way (O and l
+    // hold tiles up to t-1 here), so the result is the softmax up to rounding.
     float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
     const bool bad = !(ts <= kHi) || !(l + ts >= kLo);
     if (__builtin_amdgcn_ballot_w64(bad)) {
@@ -311,24 +346,42 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
       ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
     }
     l += ts;
+  };
 
-    // O^T += V^T P^T; the A operand of K step KS, dims 32mt.. comes from two transposing
-    // reads (keys +0..3 and +8..11 of the lane's half)
-    const char* vb = vbuf0 + (t & 1) * TL::BYTES;
-#pragma unroll
-    for (int KS = 0; KS < BK / 16; ++KS)
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const char* p0 = vb + (16 * KS + vrow) * (2 * D) + (((4 * mt) ^ vx) * 16) + vhalf;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * 2 * D));
-        const bf16x8 vf = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[KS], o[mt], 0, 0, 0);
-      }
-
-    sc[0] = sn[0];
-    sc[1] = sn[1];
+  // prologue: K0 and K1 in flight, S_0
+  dma.template tile<false, true>(0, kbuf0);
+  if (kend > 1) dma.template tile<false, true>(BK, kbuf0 + TL::BYTES);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // P_{t-1} and P_t share registers: the PV MFMAs read P_{t-1} before the exponentials of
+  // tile t overwrite it (those overlap the S_{t+1} MFMAs instead)
+  f32x16 sa[2], sb[2] = {f32x16{}, f32x16{}};
+  bf16x8 pa[4];
+  {
+    const auto s0 = qk(kbuf0);
+    sa[0] = s0[0];
+    sa[1] = s0[1];
   }
+
+  // tiles [1, fast_end) take the FAST step (two per trip, registers alternating roles):
+  // tile t is full and inside the sequence, and so is tile t + 2 (DMA without clamping)
+  const int fast_end = max(1, min(min(kfull, kend - 2), S / BK - 2));
+  int t = 0;
+  step(std::false_type{}, 0, sa, sb, pa, pa);  // S_1 -> sb, P_0 -> pa
+  t = 1;
+  for (; t + 1 < fast_end; t += 2) {
+    step(std::true_type{}, t, sb, sa, pa, pa);      // S_{t+1} -> sa, P_t -> pa
+    step(std::true_type{}, t + 1, sa, sb, pa, pa);  // S_{t+2} -> sb, P_{t+1} -> pa
+  }
+  // remaining tiles: general steps; sb holds S_t and pa holds P_{t-1} at loop entry
+  for (; t < kend; ++t) {
+    step(std::false_type{}, t, sb, sa, pa, pa);
+    for (int r = 0; r < 2; ++r) sb[r] = sa[r];
+  }
+  // last tile's P V
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  pv(vbuf0 + ((kend - 1) & 1) * TL::BYTES, pa);
 
   if (row_ok) {
     const float inv = 1.f / l;
