@@ -64,30 +64,42 @@ def allowed_pairs(segments: np.ndarray, S: int) -> int:
 
 
 def cpu_baseline(w, x, target_s=12.0):
-    """Time the oracle, as it is, on a bounded sample of the same workload: batch item 0 and
-    the query heads of as many KV groups as fit about target_s seconds (at least one)."""
+    """Time the oracle, as it is, on a bounded sample of the same workload: whole KV groups
+    (their query heads) of batch item 0, then item 1, ..., until about target_s seconds are
+    spent or the whole workload is done."""
     import oracle
     from threadpoolctl import threadpool_info
     import workloads as W
 
-    sub = W.Inputs(workload=w.replace(batch=1), q=x.q[:1], k=x.k[:1], v=x.v[:1], q_bits=None,
-                   k_bits=None, v_bits=None, w_q=x.w_q, w_k=x.w_k, positions=x.positions[:1],
-                   segments=x.segments[:1])
     group = w.n_q_heads // w.n_kv_heads
-    pairs = allowed_pairs(x.segments[0], w.seq_len)
-    heads, elapsed = 0, 0.0
-    while heads < w.n_q_heads and (heads == 0 or elapsed * (heads + group) / heads < target_s):
-        t0 = time.perf_counter()
-        oracle.hot_path(sub, heads=range(heads, heads + group))
-        elapsed += time.perf_counter() - t0
-        heads += group
+    flops, elapsed, done = 0.0, 0.0, []
+    for b in range(w.batch):
+        sub = W.Inputs(workload=w.replace(batch=1), q=x.q[b:b + 1], k=x.k[b:b + 1],
+                       v=x.v[b:b + 1], q_bits=None, k_bits=None, v_bits=None, w_q=x.w_q,
+                       w_k=x.w_k, positions=x.positions[b:b + 1],
+                       segments=x.segments[b:b + 1])
+        pairs = allowed_pairs(x.segments[b], w.seq_len)
+        heads = 0
+        while heads < w.n_q_heads:
+            if done and elapsed + elapsed / len(done) > target_s:
+                break
+            t0 = time.perf_counter()
+            oracle.hot_path(sub, heads=range(heads, heads + group))
+            elapsed += time.perf_counter() - t0
+            flops += 4.0 * w.head_dim * group * pairs
+            done.append((b, heads))
+            heads += group
+        if heads < w.n_q_heads:
+            break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    flops = 4.0 * w.head_dim * heads * pairs
+    per_item = {}
+    for b, h in done:
+        per_item[b] = per_item.get(b, 0) + group
+    what = ", ".join(f"item {b}: {n} of {w.n_q_heads} query heads" for b, n in per_item.items())
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"batch item 0, query heads 0-{heads - 1} ({heads} of {w.n_q_heads}), whole "
-                      f"path (norm, mRoPE, explicit mask, fp64 attention), {elapsed:.1f} s; "
-                      f"host os.cpu_count()={os.cpu_count()}"}
+            "sample": f"{what}; whole path per head group (norm, mRoPE, explicit mask, fp64 "
+                      f"attention), {elapsed:.1f} s; host os.cpu_count()={os.cpu_count()}"}
 
 
 def main():
