@@ -125,7 +125,11 @@ ha_status ha_rope_table_fill(double theta, int32_t head_dim, int32_t n_pos, floa
 float ha_q_prescale(const ha_attn_desc* desc);
 
 /* Tile grid used by the attention kernel for this descriptor: block_q query tokens by
- * block_k keys, n_q_blocks x n_k_blocks tiles from index 0 (last row/column ragged). */
+ * block_k keys, n_q_blocks x n_k_blocks tiles. Key tiles start at index 0 (the last one
+ * ragged). Query blocks are aligned to the end of the sequence: block qb covers rows
+ * [S - (n_q_blocks - qb) * block_q, S - (n_q_blocks - qb - 1) * block_q) clipped at 0, so
+ * the first block is the ragged one and the generation tokens that end the pages' layouts
+ * fill whole blocks. */
 ha_status ha_tile_shape(const ha_attn_desc* desc, int32_t* block_q, int32_t* block_k,
                         int32_t* n_q_blocks, int32_t* n_k_blocks);
 
@@ -136,7 +140,8 @@ ha_status ha_tile_shape(const ha_attn_desc* desc, int32_t* block_q, int32_t* blo
  *   ranges    [batch][n_q_blocks][2] int32  (kfull, kend): tiles [0, kfull) are FULL,
  *                                           [kfull, kend) PARTIAL, the rest SKIP
  *   labels    [batch][n_q_blocks][n_k_blocks] uint8 ha_tile_label       (may be NULL)
- * Over the valid part of a tile (rows and keys < seq_len): SKIP = no allowed pair,
+ * Tiles follow ha_tile_shape's grid (query blocks end-aligned).
+ * Over the valid part of a tile (rows and keys in [0, seq_len)): SKIP = no allowed pair,
  * FULL = all allowed, PARTIAL = otherwise. All DEVICE pointers, 4-byte aligned
  * (labels: any alignment). ranges may be NULL only if another output is requested. */
 ha_status ha_classify_tiles(const ha_attn_desc* desc, uint8_t* labels, int32_t* ranges,

@@ -17,7 +17,7 @@ import workloads  # noqa: E402
 
 
 def main():
-    pairs, tiles = {}, {}
+    pairs, tiles, tiles_end = {}, {}, {}
     for name, w in workloads.CONFIGS.items():
         table = workloads.segment_table(w)[0]
         M = oracle.explicit_mask(table, w.seq_len)
@@ -27,13 +27,19 @@ def main():
         tiles[name] = {"block_q": 64, "block_k": 64,
                        "skip": int((lab == 0).sum()), "full": int((lab == 1).sum()),
                        "partial": int((lab == 2).sum())}
+        lab = oracle.tile_labels(M, 64, 64, q_end_aligned=True)
+        tiles_end[name] = {"block_q": 64, "block_k": 64,
+                           "skip": int((lab == 0).sum()), "full": int((lab == 1).sum()),
+                           "partial": int((lab == 2).sum())}
     with open(os.path.join(HERE, "pair_counts.json"), "w") as f:
         json.dump({"source": "oracle.explicit_mask over workloads.CONFIGS (mask rules: HiDream-O1 "
                              "atlas 'How it works'; HunyuanImage 3.0 digest 'Generalized Causal "
                              "Attention')", "counts": pairs}, f, indent=1, sort_keys=True)
     with open(os.path.join(HERE, "tile_counts.json"), "w") as f:
-        json.dump({"source": "oracle.tile_labels(oracle.explicit_mask(...), 64, 64)",
-                   "counts": tiles}, f, indent=1, sort_keys=True)
+        json.dump({"source": "oracle.tile_labels(oracle.explicit_mask(...), 64, 64), query "
+                             "blocks from index 0 (counts) and end-aligned "
+                             "(counts_q_end_aligned)",
+                   "counts": tiles, "counts_q_end_aligned": tiles_end}, f, indent=1, sort_keys=True)
 
 
 if __name__ == "__main__":

@@ -282,19 +282,21 @@ def pin_bruteforce():
 
 
 # ---------------------------------------------------------------- tiles
-def closed_form_labels(segments, S, bq, bk):
+def closed_form_labels(segments, S, bq, bk, q_end_aligned=False):
     """Labels from per-row key limits: a causal row i sees [0, i+1), a full row [0, S),
     an image row [0, end of its segment). Every row is a prefix, so per query block
     tiles below floor(min lim / bk) are FULL (all of them if min lim = S), tiles from
-    ceil(max lim / bk) on are SKIP, and the rest PARTIAL."""
+    ceil(max lim / bk) on are SKIP, and the rest PARTIAL. Query blocks start at row 0, or
+    at S - nq * bq (clipped at 0) when end-aligned."""
     lim = np.empty(S, dtype=np.int64)
     for a, L, kind in segments:
         i = np.arange(a, a + L)
         lim[a:a + L] = i + 1 if kind == C else (S if kind == F else a + L)
     nq, nk = -(-S // bq), -(-S // bk)
+    q0 = S - nq * bq if q_end_aligned else 0
     out = np.empty((nq, nk), dtype=np.uint8)
     for qb in range(nq):
-        l = lim[qb * bq:(qb + 1) * bq]
+        l = lim[max(q0 + qb * bq, 0):q0 + (qb + 1) * bq]
         kfull = nk if l.min() >= S else l.min() // bk
         kend = -(-l.max() // bk)
         out[qb] = [1 if kb < kfull else (2 if kb < kend else 0) for kb in range(nk)]
@@ -302,13 +304,16 @@ def closed_form_labels(segments, S, bq, bk):
 
 
 def pin_tile_labels():
-    gold = json.load(open(os.path.join(GOLDEN, "tile_counts.json")))["counts"]
+    gold = json.load(open(os.path.join(GOLDEN, "tile_counts.json")))
     for name, w in W.CONFIGS.items():
         table = W.segment_table(w)[0]
         M = oracle.mask.explicit_mask(table, w.seq_len)
-        for bq, bk in ((64, 64), (128, 64), (32, 64)):
-            lab = oracle.tile_labels(M, bq, bk)
-            assert np.array_equal(lab, closed_form_labels(table, w.seq_len, bq, bk)), (name, bq)
-        lab = oracle.tile_labels(M, 64, 64)
-        assert [int((lab == t).sum()) for t in (0, 1, 2)] == [
-            gold[name]["skip"], gold[name]["full"], gold[name]["partial"]], name
+        for end in (False, True):
+            for bq, bk in ((64, 64), (128, 64), (32, 64), (96, 64)):
+                lab = oracle.tile_labels(M, bq, bk, q_end_aligned=end)
+                want = closed_form_labels(table, w.seq_len, bq, bk, q_end_aligned=end)
+                assert np.array_equal(lab, want), (name, bq, end)
+            key = "counts_q_end_aligned" if end else "counts"
+            lab = oracle.tile_labels(M, 64, 64, q_end_aligned=end)
+            assert [int((lab == t).sum()) for t in (0, 1, 2)] == [
+                gold[key][name]["skip"], gold[key][name]["full"], gold[key][name]["partial"]], name

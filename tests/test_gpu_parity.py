@@ -77,7 +77,7 @@ def check_labels(w, segments):
     (bq, bk), labels, ranges, lim = classify(w, segments)
     for b in range(w.batch):
         M = oracle.explicit_mask(segments[b], w.seq_len)
-        want = oracle.tile_labels(M, bq, bk)
+        want = oracle.tile_labels(M, bq, bk, q_end_aligned=True)
         assert np.array_equal(labels[b], want), f"batch {b}: tile labels differ"
         assert np.array_equal(lim[b], M.sum(axis=1)), f"batch {b}: row limits differ"
         kfull = (want == 1).sum(axis=1)
@@ -283,24 +283,41 @@ def test_prologue_q_out_scale(name):
     assert (np.abs(f64(ko) - k_ref) <= tol(k_ref)).all()
 
 
-@pytest.mark.parametrize("sign", [1.0, -1.0])
+@pytest.mark.parametrize("alpha,sign", [(16.0, 1.0), (26.0, 1.0), (36.0, -1.0)])
 @pytest.mark.parametrize("prescaled", [False, True])
-def test_extreme_logits_take_the_rescale_path(sign, prescaled):
-    """Scores far above (sign +1, about +33 in log2 units) or far below (sign -1, about
-    -165, where every exp2 underflows even as a denormal) the initial reference force the
-    re-reference path. q and k share a strong common direction e_0, which shifts each row by
-    a constant, so the softmax itself stays well conditioned. (A prescaled q is rounded
-    after the scale, so its error grows with the common component; 36 keeps it small.)"""
+def test_extreme_logits(alpha, sign, prescaled):
+    """q and k share a strong common direction e_0, which shifts every score of a row by
+    about sign * alpha^2 * scale * log2(e): +33, +86 or -165 in log2 units for alpha 16, 26
+    and 36 at head dim 128, so the softmax itself stays well conditioned. +33 stays on the
+    fast path with huge P values; +86 (tile sums beyond 2^64) and -165 (every exp2
+    underflows, even as a denormal) force the careful re-referencing pass. (A prescaled q
+    is rounded after the scale, so its error grows with the common component.)"""
     w = small([W.Segment(C, 40), W.Segment(F, 100), W.Segment(G, 61)], rope="none", norm=False,
               hq=8, hkv=2)
     x = W.generate(w)
-    alpha = 16.0 if sign > 0 else 36.0
     x.q[..., 0] += sign * alpha
     x.k[..., 0] += alpha
     refresh_bits(x)
     dev = to_device(x)
     got = f64(planned(x, dev, prescaled))
-    compare(got, oracle.hot_path(x), "bf16", f"extreme logits sign {sign} prescaled {prescaled}")
+    compare(got, oracle.hot_path(x), "bf16", f"extreme logits {sign * alpha} prescaled {prescaled}")
+
+
+def test_extreme_logits_late_keys_one_head():
+    """Only query head 3 and only keys from 130 on carry the common direction: the rows of
+    that head leave the range at their third key tile, after two ordinary tiles, while
+    every other head of the work item stays in range; the whole work item is redone on the
+    careful pass and must still match."""
+    w = small([W.Segment(C, 40), W.Segment(F, 100), W.Segment(G, 61)], rope="none", norm=False,
+              hq=8, hkv=2)
+    x = W.generate(w)
+    x.q[:, :, 3, 0] += 26.0
+    x.k[:, 130:, :, 0] += 26.0
+    refresh_bits(x)
+    dev = to_device(x)
+    for prescaled in (False, True):
+        got = f64(planned(x, dev, prescaled))
+        compare(got, oracle.hot_path(x), "bf16", f"late extreme keys, one head, prescaled {prescaled}")
 
 
 def test_per_batch_layouts_differ():

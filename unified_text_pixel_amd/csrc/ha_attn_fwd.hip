@@ -210,9 +210,10 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   const int h = g * G + hg;
   const int hi = lane >> 5;
   const int S = a.S;
-  const int i = qb * C::BQ + tsub * 32 + (lane & 31);
-  const bool row_ok = i < S;
-  const int ic = row_ok ? i : S - 1;
+  // query blocks end at S (the first block of the sequence is the ragged one)
+  const int i = S - (a.nq - qb) * C::BQ + tsub * 32 + (lane & 31);
+  const bool row_ok = i >= 0;
+  const int ic = row_ok ? i : 0;
   const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : S;
   const int kfull = a.ranges[((int64_t)b * a.nq + qb) * 2 + 0];
   const int kend = a.ranges[((int64_t)b * a.nq + qb) * 2 + 1];
@@ -422,9 +423,10 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
   const int h = g * G + hg;
   const int hi = lane >> 5;
   const int S = a.S;
-  const int i = qb * C::BQ + tsub * 32 + (lane & 31);
-  const bool row_ok = i < S;
-  const int ic = row_ok ? i : S - 1;
+  // query blocks end at S (the first block of the sequence is the ragged one)
+  const int i = S - (a.nq - qb) * C::BQ + tsub * 32 + (lane & 31);
+  const bool row_ok = i >= 0;
+  const int ic = row_ok ? i : 0;
   const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : S;
   const int kfull = a.ranges[((int64_t)b * a.nq + qb) * 2 + 0];
   const int kend = a.ranges[((int64_t)b * a.nq + qb) * 2 + 1];

@@ -7,7 +7,10 @@
 // because {j <= i} together with the row's own segment [s0, e0) (which contains i) is
 // [0, e0). (HiDream-O1 atlas page, "How it works"; hidream-o1-p100a model card, "What
 // this model is"; HunyuanImage 3.0 digest, "Generalized Causal Attention".)
-// With prefixes, the tiles of one query block are FULL on [0, kfull), PARTIAL on
+// Query blocks are aligned to the end of the sequence (the first block is the ragged one),
+// where the pages' layouts put the generation tokens that carry almost all of the work, so
+// those rows fill whole blocks. With prefixes, the tiles of one query block are FULL on
+// [0, kfull), PARTIAL on
 // [kfull, kend) and SKIP beyond, where kfull comes from the block's smallest limit and
 // kend from its largest; the classifier writes those two integers, the per-row limits
 // and, on request, the explicit per-tile labels.
@@ -32,8 +35,9 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyArgs a) {
   }
   __syncthreads();
 
-  const int r0 = qb * a.bq;
-  const int r1 = min(S, r0 + a.bq);
+  // query blocks are cut back from the end of the sequence: the first one is ragged
+  const int r1 = S - (a.nq - 1 - qb) * a.bq;
+  const int r0 = max(0, r1 - a.bq);
   int lo = S, hi = 0;
   for (int i = r0 + threadIdx.x; i < r1; i += kThreads) {
     int lim = i + 1;
