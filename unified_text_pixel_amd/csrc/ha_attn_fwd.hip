@@ -44,7 +44,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr float kHi = 1048576.0f;             // 2^20: largest tile row sum taken as is
+constexpr float kHi = 18446744073709551616.0f;  // 2^64: largest tile row sum taken as is
 constexpr float kLo = 8.673617379884035e-19f; // 2^-60: smallest running row sum taken as is
 constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -198,9 +198,13 @@ template <int D, int G, bool PRE>
 __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   using C = CfgB<D, G>;
   using TL = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char lds[4 * TL::BYTES];  // K0 K1 V0 V1
-  char* const kbuf0 = lds;
-  char* const vbuf0 = lds + 2 * TL::BYTES;
+  // K and V double buffers as four distinct arrays: a read of one buffer then never waits
+  // for DMA still landing in another (the compiler tracks LDS DMA per array)
+  __shared__ __attribute__((aligned(1024))) char k0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[TL::BYTES];
+  __shared__ int redo;  // some row left the range on the main pass: redo the work item
 
   const Item it = work_item(a);
   const int b = it.b, g = it.g, qb = it.qb;
@@ -232,15 +236,15 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   const int vx = vclow ^ TL::vswz(vrow);  // chunk 4mt + vclow sits at (4mt) ^ vx
   const int vhalf = 8 * (t16 & 1);
 
-  // Softmax state of this lane's row, in log2 units: reference m (not necessarily the
-  // running max) and l = sum of exp2(score - m) over the row's keys seen so far. A row
-  // lives in two lanes (one per 16-key half of every 32 keys) whose O^T registers hold
-  // different output dims accumulated from both halves' P, so the row's state is kept
-  // whole in both lanes (tile sums are reduced over the pair). negm holds -m in the
-  // units of the S accumulator (log2 units when q is prescaled, raw otherwise) and is
-  // the C operand of each tile's first MFMA, so the subtraction costs nothing.
-  float m = 0.f, l = 0.f;
-  f32x16 negm = f32x16{};
+  // Softmax state of this lane's row, in log2 units: reference m and l = sum of
+  // exp2(score - m) over the row's keys seen so far. A row lives in two lanes (one per
+  // 16-key half of every 32 keys) whose O^T registers hold different output dims
+  // accumulated from both halves' P, so the row's state is kept whole in both lanes (tile
+  // sums are reduced over the pair). The main pass keeps m = 0 throughout: P = exp2(S)
+  // needs no subtraction and no running max. A lane only records whether a tile sum of
+  // its row left [kLo, kHi] (or was not finite); if any did, the work item is redone on
+  // a careful pass that re-references (below).
+  float l = 0.f;
   f32x16 o[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
@@ -250,8 +254,9 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * hi);
 
-  // S^T - m for the 64 keys of a K buffer, the two 32-key halves interleaved
-  auto qk = [&](const char* kbuf) {
+  // S^T + c0 for the 64 keys of a K buffer, the two 32-key halves interleaved (c0 is the
+  // C operand of the first MFMA: zero, or -m on the careful pass)
+  auto qk = [&](const char* kbuf, const f32x16& c0) {
     std::array<f32x16, 2> s;
     const char* r0 = kbuf + krow * (2 * D);
 #pragma unroll
@@ -259,14 +264,15 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
       const int off = ((2 * kk) ^ kx) * 16;
       const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(r0 + off);
       const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(r0 + 32 * 2 * D + off);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], kk == 0 ? negm : s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], kk == 0 ? negm : s[1], 0, 0, 0);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], kk == 0 ? c0 : s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], kk == 0 ? c0 : s[1], 0, 0, 0);
     }
     return s;
   };
 
   // Masks tile t of S (keys >= lim) where the tile is partial or runs past the end.
   auto mask = [&](f32x16 (&sc)[2], int t) {
+    if (t < kfull && (t + 1) * BK <= S) return;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -291,67 +297,42 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
       }
   };
 
-  // One pipeline step for tile t: land K_{t+1} and V_{t-1}, start the DMA of K_{t+2} and
-  // V_t, then S_{t+1} = K_{t+1} Q^T - m, O += V_{t-1} P_{t-1} and P_t = exp2(S_t - m).
-  // FAST steps (tiles t-1 .. t+2 present, tiles t .. t+2 full and inside the sequence)
-  // have no branch before the re-reference check, so those two MFMA chains and the
-  // exponentials are free to interleave.
-  auto step = [&](auto fast_tag, int t, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pfp)[4],
-                  bf16x8 (&pf)[4]) {
+  // One main-pass step for tile t: land K_{t+1} and V_{t-1}, start the DMA of K_{t+2}
+  // and V_t, then S_{t+1} = K_{t+1} Q^T, O += V_{t-1} P_{t-1} and P_t = exp2(S_t). Tile
+  // j sits in buffer j mod 2 (PAR = t mod 2, known at compile time). FAST steps (tiles
+  // t-1 .. t+2 present, tiles t .. t+2 full and inside the sequence) have no branch at
+  // all, so the two MFMA chains and the exponentials interleave freely.
+  bool off_range = false;
+  auto step = [&](auto fast_tag, auto par_tag, int t, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  bf16x8 (&pfp)[4], bf16x8 (&pf)[4]) {
     constexpr bool FAST = decltype(fast_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    char* const kw = PAR ? k1 : k0;        // K_t, free now: receives K_{t+2}
+    const char* const kr = PAR ? k0 : k1;  // K_{t+1}
+    char* const vw = PAR ? v1 : v0;        // receives V_t
+    const char* const vr = PAR ? v0 : v1;  // V_{t-1}
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (FAST || t + 2 < kend) dma.template tile<false, !FAST>((t + 2) * BK, kbuf0 + (t & 1) * TL::BYTES);
-    dma.template tile<true, !FAST>(t * BK, vbuf0 + (t & 1) * TL::BYTES);
+    if (FAST || t + 2 < kend) dma.template tile<false, !FAST>((t + 2) * BK, kw);
+    dma.template tile<true, !FAST>(t * BK, vw);
     if (FAST || t + 1 < kend) {
-      const auto s1 = qk(kbuf0 + ((t + 1) & 1) * TL::BYTES);
+      const auto s1 = qk(kr, f32x16{});
       sn[0] = s1[0];
       sn[1] = s1[1];
     }
-    if (FAST || t >= 1) pv(vbuf0 + ((t - 1) & 1) * TL::BYTES, pfp);
-    if (!FAST && (t >= kfull || (t + 1) * BK > S)) mask(sc, t);
-
-    // Fast path: P = exp2(S - m) as is. It is taken unless some row's tile sum leaves
-    // [kLo, kHi] (or is not finite); those rows are first re-referenced to the larger of
-    // the tile max and log2(l), so both the old sum and the new tile end up <= 1 with one
-    // of them near 1. Numerator and denominator share the reference either way (O and l
-    // hold tiles up to t-1 here), so the result is the softmax up to rounding.
-    float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
-    const bool bad = !(ts <= kHi) || !(l + ts >= kLo);
-    if (__builtin_amdgcn_ballot_w64(bad)) {
-      float mx = sc[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-      mx = wave_pair_max(mx);
-      if (!PRE) mx *= c;
-      float sh = fmaxf(mx, __builtin_amdgcn_logf(l));
-      sh = (bad && sh > -INFINITY) ? sh : 0.f;
-      m += sh;
-      // alpha <= 1/l for l > 0 (sh >= log2 l), and l >= 2^-60 outside the first tile, so
-      // it cannot overflow; with l = 0 nothing has been accumulated (O = 0) and it is 0
-      const float alpha = l == 0.f ? 0.f : __builtin_amdgcn_exp2f(-sh);
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
-      l *= alpha;
-      const float shs = PRE ? sh : sh / c;  // in accumulator units
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        negm[r] -= shs;
-        sc[0][r] -= shs;
-        sc[1][r] -= shs;
-        sn[0][r] -= shs;  // S_{t+1} was computed against the old reference
-        sn[1][r] -= shs;
-      }
-      ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
-    }
+    if (FAST || t >= 1) pv(vr, pfp);
+    if (!FAST) mask(sc, t);
+    const float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
+    off_range = off_range || !(ts <= kHi) || !(l + ts >= kLo);
     l += ts;
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
 
-  // prologue: K0 and K1 in flight, S_0
-  dma.template tile<false, true>(0, kbuf0);
-  if (kend > 1) dma.template tile<false, true>(BK, kbuf0 + TL::BYTES);
+  if (tid == 0) redo = 0;
+  // prologue: K0 and K1 in flight, S_0 (the barrier also publishes redo = 0)
+  dma.template tile<false, true>(0, k0);
+  if (kend > 1) dma.template tile<false, true>(BK, k1);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // P_{t-1} and P_t share registers: the PV MFMAs read P_{t-1} before the exponentials of
@@ -359,30 +340,86 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   f32x16 sa[2], sb[2] = {f32x16{}, f32x16{}};
   bf16x8 pa[4];
   {
-    const auto s0 = qk(kbuf0);
+    const auto s0 = qk(k0, f32x16{});
     sa[0] = s0[0];
     sa[1] = s0[1];
   }
 
-  // tiles [1, fast_end) take the FAST step (two per trip, registers alternating roles):
-  // tile t is full and inside the sequence, and so is tile t + 2 (DMA without clamping)
+  // tiles [1, fast_end) take the FAST step: tile t is full and inside the sequence, and
+  // so is tile t + 2 (DMA without clamping). Both loops take two steps per trip (odd t,
+  // then even), the S registers alternating roles; sb holds S_t when a trip starts.
   const int fast_end = max(1, min(min(kfull, kend - 2), S / BK - 2));
-  int t = 0;
-  step(std::false_type{}, 0, sa, sb, pa, pa);  // S_1 -> sb, P_0 -> pa
-  t = 1;
+  step(std::false_type{}, P0{}, 0, sa, sb, pa, pa);  // S_1 -> sb, P_0 -> pa
+  int t = 1;
   for (; t + 1 < fast_end; t += 2) {
-    step(std::true_type{}, t, sb, sa, pa, pa);      // S_{t+1} -> sa, P_t -> pa
-    step(std::true_type{}, t + 1, sa, sb, pa, pa);  // S_{t+2} -> sb, P_{t+1} -> pa
+    step(std::true_type{}, P1{}, t, sb, sa, pa, pa);      // S_{t+1} -> sa, P_t -> pa
+    step(std::true_type{}, P0{}, t + 1, sa, sb, pa, pa);  // S_{t+2} -> sb, P_{t+1} -> pa
   }
-  // remaining tiles: general steps; sb holds S_t and pa holds P_{t-1} at loop entry
-  for (; t < kend; ++t) {
-    step(std::false_type{}, t, sb, sa, pa, pa);
-    for (int r = 0; r < 2; ++r) sb[r] = sa[r];
+  for (; t + 1 < kend; t += 2) {
+    step(std::false_type{}, P1{}, t, sb, sa, pa, pa);
+    step(std::false_type{}, P0{}, t + 1, sa, sb, pa, pa);
   }
+  if (t < kend) step(std::false_type{}, P1{}, t, sb, sa, pa, pa);
   // last tile's P V
+  if (__builtin_amdgcn_ballot_w64(off_range)) redo = 1;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  pv(vbuf0 + ((kend - 1) & 1) * TL::BYTES, pa);
+  pv(((kend - 1) & 1) ? v1 : v0, pa);
+
+  // Careful pass, only when some row of the work item left the range: every wave starts
+  // over, one tile at a time, and re-references rows whose tile sum leaves [kLo, kHi] to
+  // the larger of the tile max and log2(l), so both the old sum and the new tile end up
+  // <= 1 with one of them near 1. Numerator and denominator share the reference either
+  // way, so the result is the softmax up to rounding. negm holds -m in the units of the S
+  // accumulator (log2 units when q is prescaled, raw otherwise) and is the C operand of
+  // each tile's first MFMA.
+  if (redo) {
+    float m = 0.f;
+    f32x16 negm = f32x16{};
+    l = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
+    for (int u = 0; u < kend; ++u) {
+      __syncthreads();  // every wave is done with the buffers
+      dma.template tile<false, true>(u * BK, k0);
+      dma.template tile<true, true>(u * BK, v0);
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const auto s0 = qk(k0, negm);
+      f32x16 sc[2] = {s0[0], s0[1]};
+      mask(sc, u);
+      float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pa));
+      const bool bad = !(ts <= kHi) || !(l + ts >= kLo);
+      if (__builtin_amdgcn_ballot_w64(bad)) {
+        float mx = sc[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+        mx = wave_pair_max(mx);
+        if (!PRE) mx *= c;
+        float sh = fmaxf(mx, __builtin_amdgcn_logf(l));
+        sh = (bad && sh > -INFINITY) ? sh : 0.f;
+        m += sh;
+        // alpha <= 1/l for l > 0 (sh >= log2 l), and l >= kLo outside the first tile, so
+        // it cannot overflow; with l = 0 nothing has been accumulated (O = 0) and it is 0
+        const float alpha = l == 0.f ? 0.f : __builtin_amdgcn_exp2f(-sh);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
+        l *= alpha;
+        const float shs = PRE ? sh : sh / c;  // in accumulator units
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          negm[r] -= shs;
+          sc[0][r] -= shs;
+          sc[1][r] -= shs;
+        }
+        ts = wave_pair_sum(exp_tile<PRE>(sc, c, pa));
+      }
+      l += ts;
+      pv(v0, pa);
+    }
+  }
 
   if (row_ok) {
     const float inv = 1.f / l;
