@@ -161,7 +161,12 @@ def test_tile_shape():
     assert U.ha_tile_shape(desc()) == (32, 64, 3, 2)
     d = desc(batch=2, seq_len=4354, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
              segments=seg([[0, 258, 0], [258, 4096, 1]], 2))
-    assert U.ha_tile_shape(d) == (32, 64, 137, 69)
+    assert U.ha_tile_shape(d) == (64, 64, 69, 69)
+    # bf16: eight waves of 32 rows over the G query heads of a KV head
+    for g, bq in ((1, 256), (2, 128), (4, 64), (8, 32)):
+        d = desc(n_q_heads=8, n_kv_heads=8 // g, dtype="bf16")
+        assert U.ha_tile_shape(d)[0] == bq
+    # fp32: four waves
     for g, bq in ((1, 128), (2, 64), (8, 32)):
         d = desc(n_q_heads=8, n_kv_heads=8 // g)
         assert U.ha_tile_shape(d)[0] == bq
@@ -185,5 +190,5 @@ def test_workspace_layout():
              segments=seg([[0, 258, 0], [258, 4096, 1]], 2))
     plain = U.ha_attn_workspace_bytes(d)
     with_pro = U.ha_attn_workspace_bytes(d, U.PrologueDesc("none"))
-    assert plain >= 2 * 4354 * 4 + 2 * 137 * 8
+    assert plain >= 2 * 4354 * 4 + 2 * 69 * 8
     assert with_pro - plain >= 2 * 4354 * 40 * 128 * 2

@@ -8,9 +8,9 @@
 // this model is"; HunyuanImage 3.0 digest, "Generalized Causal Attention". GQA 32/8,
 // head dim 128: model card architecture paragraph.)
 //
-// Work item: one (batch, KV head, query block). Its waves cover the G query heads that
-// share the KV head, 32 query rows per wave, so every K/V tile staged in LDS serves all
-// G heads. Per 64-key tile each wave computes
+// Work item: one (batch, KV head, query block). Its eight waves (two per SIMD) cover the G
+// query heads that share the KV head, 32 query rows per wave, 256 / G rows per block, so
+// every K/V tile staged in LDS serves all of them. Per 64-key tile each wave computes
 //   S^T (keys x rows)  = K Q^T   with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q)
 //   O^T (dims x rows) += V^T P^T with the same instruction    (A = V^T from LDS, B = P)
 // In this orientation one lane holds one query row (lane % 32) and 16 of every 32 keys
@@ -20,13 +20,16 @@
 //
 // bf16 pipeline (one barrier per key tile):
 //  - K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4, no
-//    registers); K runs two tiles ahead and V one, in two buffers each.
-//  - S for tile t+1 is computed while the exponentials of tile t run.
+//    registers); K runs two tiles ahead and V one, in two buffers each (four distinct
+//    LDS arrays).
+//  - Step t computes S_{t+1}, O += V_{t-1} P_{t-1} and P_t = exp2(S_t): the exponentials
+//    interleave with both MFMA chains.
 //  - V stays row-major in LDS; ds_read_b64_tr_b16 gathers the transposed A operand.
 //  - Both tiles are XOR-swizzled on 16-byte chunks so the reads are bank-conflict free.
-// Softmax: q arrives prescaled by scale*log2(e) (or the scale is applied here), -m enters
-// as the C operand of the first MFMA, P = exp2(S - m) is taken as is, and only when a
-// row's tile sum leaves [2^-60, 2^20] is the row re-referenced (exactly; see below).
+// Softmax: q arrives prescaled by scale*log2(e) (or the scale is applied here) and the
+// main pass keeps the reference at 0, P = exp2(S) taken as is; a work item in which some
+// row's tile sum leaves [2^-60, 2^64] is redone on a careful pass that re-references
+// (exactly; see below).
 // fp32 inputs use a plain variant (fp32 P, v_mfma_f32_32x32x2_f32, running max).
 #include <array>
 #include <type_traits>
@@ -50,8 +53,10 @@ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int BK = kBlockK;
 
-// 32-row slices per query head in one work item
-constexpr int tsub_for(int group) { return group == 1 ? 4 : (group == 2 ? 2 : 1); }
+// 32-row slices per query head in one work item: bf16 uses eight waves (two per SIMD, so
+// every K/V tile staged in LDS serves 8 x 32 query rows), fp32 four
+constexpr int tsub_for(int group) { return 8 / group; }
+constexpr int tsub_f32(int group) { return group == 1 ? 4 : (group == 2 ? 2 : 1); }
 
 __device__ inline float wave_pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
@@ -335,10 +340,9 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   if (kend > 1) dma.template tile<false, true>(BK, k1);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  // P_{t-1} and P_t share registers: the PV MFMAs read P_{t-1} before the exponentials of
-  // tile t overwrite it (those overlap the S_{t+1} MFMAs instead)
+  // P_t sits in register set t mod 2 (pa, pb)
   f32x16 sa[2], sb[2] = {f32x16{}, f32x16{}};
-  bf16x8 pa[4];
+  bf16x8 pa[4], pb[4];
   {
     const auto s0 = qk(k0, f32x16{});
     sa[0] = s0[0];
@@ -349,22 +353,25 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // so is tile t + 2 (DMA without clamping). Both loops take two steps per trip (odd t,
   // then even), the S registers alternating roles; sb holds S_t when a trip starts.
   const int fast_end = max(1, min(min(kfull, kend - 2), S / BK - 2));
-  step(std::false_type{}, P0{}, 0, sa, sb, pa, pa);  // S_1 -> sb, P_0 -> pa
+  step(std::false_type{}, P0{}, 0, sa, sb, pb, pa);  // S_1 -> sb, P_0 -> pa
   int t = 1;
   for (; t + 1 < fast_end; t += 2) {
-    step(std::true_type{}, P1{}, t, sb, sa, pa, pa);      // S_{t+1} -> sa, P_t -> pa
-    step(std::true_type{}, P0{}, t + 1, sa, sb, pa, pa);  // S_{t+2} -> sb, P_{t+1} -> pa
+    step(std::true_type{}, P1{}, t, sb, sa, pa, pb);      // S_{t+1} -> sa, P_t -> pb
+    step(std::true_type{}, P0{}, t + 1, sa, sb, pb, pa);  // S_{t+2} -> sb, P_{t+1} -> pa
   }
   for (; t + 1 < kend; t += 2) {
-    step(std::false_type{}, P1{}, t, sb, sa, pa, pa);
-    step(std::false_type{}, P0{}, t + 1, sa, sb, pa, pa);
+    step(std::false_type{}, P1{}, t, sb, sa, pa, pb);
+    step(std::false_type{}, P0{}, t + 1, sa, sb, pb, pa);
   }
-  if (t < kend) step(std::false_type{}, P1{}, t, sb, sa, pa, pa);
+  if (t < kend) step(std::false_type{}, P1{}, t, sb, sa, pa, pb);
   // last tile's P V
   if (__builtin_amdgcn_ballot_w64(off_range)) redo = 1;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  pv(((kend - 1) & 1) ? v1 : v0, pa);
+  if ((kend - 1) & 1)
+    pv(v1, pb);
+  else
+    pv(v0, pa);
 
   // Careful pass, only when some row of the work item left the range: every wave starts
   // over, one tile at a time, and re-references rows whose tile sum leaves [kLo, kHi] to
@@ -440,7 +447,7 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
 // registers into padded LDS rows, v_mfma_f32_32x32x2_f32 for both products.
 template <int D, int G>
 struct CfgF {
-  static constexpr int TSUB = tsub_for(G);
+  static constexpr int TSUB = tsub_f32(G);
   static constexpr int NW = G * TSUB;
   static constexpr int NT = NW * 64;
   static constexpr int BQ = 32 * TSUB;
@@ -577,8 +584,7 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
 
 int attn_block_q(int head_dim, int group, bool f32) {
   (void)head_dim;
-  (void)f32;
-  return 32 * tsub_for(group);
+  return 32 * (f32 ? tsub_f32(group) : tsub_for(group));
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
