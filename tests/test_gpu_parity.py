@@ -186,6 +186,66 @@ def test_full_size_sampled_rows(name):
     assert np.array_equal(got[:, 0], np.repeat(v0, w.n_q_heads // w.n_kv_heads, axis=1))
 
 
+def test_long_sequence_sampled_rows():
+    """A 4096^2 HiDream-style image: 258 causal tokens then a 128 x 128 grid of full rows
+    (S = 16642, 261 key tiles per generation row), batch 1, sampled rows against the
+    oracle; large grids, long key loops and wide indices."""
+    w = W.get_config("hd2048").replace(
+        name="hd4096", batch=1,
+        segments=(W.Segment(C, 258), W.Segment(F, 128 * 128, (128, 128))))
+    x = W.generate(w)
+    out, _ = run_fwd(x)
+    got = f64(out)
+    rows = sample_rows(w, n_random=24)
+    heads = list(range(0, w.n_q_heads, 3))
+    want = oracle.hot_path_rows(x, 0, rows, heads)
+    compare(got[0, rows][:, heads], want, w.dtype, f"hd4096 ({len(rows)} rows x {len(heads)} heads)")
+
+
+def test_max_segment_count():
+    """64 segments per item (the most a table may hold), random kinds and lengths, image
+    segments side by side, two items with different tables: whole output against the
+    oracle."""
+    rng = np.random.default_rng(11)
+    kinds = [C, F, G]
+    S = 700
+    segs = []
+    for b in range(2):
+        lens = rng.integers(1, 11, size=64)
+        lens[-1] += S - lens.sum()
+        at, rows = 0, []
+        for L, k in zip(lens, rng.integers(0, 3, size=64)):
+            rows.append([at, int(L), kinds[int(k)]])
+            at += int(L)
+        segs.append(rows)
+    seg = np.array(segs, dtype=np.int32)
+    w = small([W.Segment(C, S)], batch=2, rope="1d")
+    x = W.generate(w)
+    x.segments = seg
+    check_labels(w, seg)
+    out, _ = run_fwd(x)
+    compare(f64(out), oracle.hot_path(x), "bf16", "64 segments")
+
+
+def test_careful_pass_full_size_shape():
+    """The hd1024 layout at full size with every score of query head 5 shifted by about +86
+    log2 units from key 300 on: the work items of that head's KV group take the careful
+    pass across all of their tiles; sampled rows against the oracle. Without a rotary
+    embedding the shift is the same for every key of a row, so the bf16 rounding of the
+    large prescaled q component cancels in the softmax (with rotation it would not, and the
+    comparison would measure bf16 conditioning instead of the careful pass)."""
+    w = W.get_config("hd1024").replace(qk_norm=False, batch=1, rope="none")
+    x = W.generate(w)
+    x.q[:, :, 5, 0] += 26.0
+    x.k[:, 300:, :, 0] += 26.0
+    out, _ = run_fwd(refresh_bits(x))
+    got = f64(out)
+    rows = sample_rows(w, n_random=16)
+    heads = [4, 5, 6, 7, 12]
+    want = oracle.hot_path_rows(x, 0, rows, heads)
+    compare(got[0, rows][:, heads], want, w.dtype, f"careful pass at hd1024 shape")
+
+
 def uniform_probe(w):
     """q = 0 makes every allowed weight exactly 1 (RMSNorm and rotary of 0 are 0), masked
     ones exactly 0; with v_j one-hot on channel (j // 64) mod d the output channel c of row
