@@ -14,6 +14,7 @@ What it computes, slowly and plainly, in float64 unless a function says otherwis
   tiles.py      tile labels SKIP / FULL / PARTIAL by brute force over the mask
   pipeline.py   the whole path in the pages' order: norm, rotary, mask, attention
   brute.py      scalar pure-Python fp64 re-derivation for tiny inputs
+  backward.py   gradients of the whole path (attention, rotary, norm) and the row lse
 
 Parity pins (tests/test_oracle_*.py) tie each part to something other than itself:
 closed-form allowed-pair counts, library routines (torch CPU scaled_dot_product_attention
@@ -29,6 +30,8 @@ from .rope import inv_freq, axis_of_pair, rope_angles, apply_rope
 from .masked_attention import attention, attention_rows
 from .tiles import tile_labels
 from .pipeline import prologue, hot_path, hot_path_rows
+from .backward import (attention_lse, attention_backward, rope_backward, rms_norm_backward,
+                       path_lse, path_backward)
 
 SEG_CAUSAL, SEG_FULL, SEG_GCA = 0, 1, 2
 LABEL_SKIP, LABEL_FULL, LABEL_PARTIAL = 0, 1, 2

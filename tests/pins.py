@@ -317,3 +317,105 @@ def pin_tile_labels():
             lab = oracle.tile_labels(M, 64, 64, q_end_aligned=end)
             assert [int((lab == t).sum()) for t in (0, 1, 2)] == [
                 gold[key][name]["skip"], gold[key][name]["full"], gold[key][name]["partial"]], name
+
+# ---------------------------------------------------------------- backward (oracle/backward.py)
+
+def _bwd_layout(rope="mrope", norm=True, batch=1, seed=21):
+    """Tiny layout with every segment kind: text, a 2x2 full (HiDream generation) block,
+    a 2x2 image (GCA) block, more text."""
+    segs = [W.Segment(C, 3), W.Segment(F, 4, (2, 2)), W.Segment(G, 4, (2, 2)), W.Segment(C, 2)]
+    return small_workload(segs, hq=4, hkv=2, d=8, rope=rope, sections=(2, 1, 1), norm=norm,
+                          batch=batch, seed=seed)
+
+
+def pin_backward_finite_differences():
+    """Brute force: central differences of the forward path (pinned on its own by the pins
+    above) agree with the backward for entries of q, k, v and both norm weights."""
+    import dataclasses
+    import oracle.backward
+    w = _bwd_layout(batch=2)
+    x = W.generate(w)
+    rng = np.random.default_rng(5)
+    dout = rng.standard_normal((w.batch, w.seq_len, w.n_q_heads, w.head_dim))
+    g = oracle.backward.path_backward(x, dout)
+
+    def loss(name, arr):
+        y = dataclasses.replace(x, **{name: arr})
+        return float(np.sum(oracle.pipeline.hot_path(y) * dout))
+
+    h = 1e-5
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("w_q", "dw_q"), ("w_k", "dw_k")):
+        base = np.asarray(getattr(x, name), dtype=np.float64)
+        for i in rng.choice(base.size, size=min(8, base.size), replace=False):
+            up, dn = base.copy(), base.copy()
+            up.flat[i] += h
+            dn.flat[i] -= h
+            num = (loss(name, up) - loss(name, dn)) / (2 * h)
+            got = g[key].flat[i]
+            assert abs(num - got) <= 1e-6 * max(1.0, abs(num)), (name, int(i), num, got)
+
+
+def pin_backward_autograd():
+    """torch autograd (fp64, CPU) through F.rms_norm, a rotation and F.scaled_dot_product_
+    attention with the boolean mask gives the same gradients as the oracle's formulas."""
+    import oracle.backward
+    for rope, norm in (("mrope", True), ("2d", False), ("none", True)):
+        w = _bwd_layout(rope=rope, norm=norm, seed=22)
+        x = W.generate(w)
+        B, S, Hq, d = x.q.shape
+        grp = Hq // w.n_kv_heads
+        rng = np.random.default_rng(6)
+        dout = rng.standard_normal((B, S, Hq, d))
+        T = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+        q, k, v = T(x.q), T(x.k), T(x.v)
+        wq = T(x.w_q) if norm else None
+        wk = T(x.w_k) if norm else None
+        qn = torch.nn.functional.rms_norm(q, (d,), wq, w.norm_eps) if norm else q
+        kn = torch.nn.functional.rms_norm(k, (d,), wk, w.norm_eps) if norm else k
+        if rope != "none":
+            axes = oracle.rope.axis_of_pair(rope, d, w.mrope_sections)
+            ang = torch.tensor(oracle.rope.rope_angles(x.positions, axes,
+                                                       oracle.rope.inv_freq(w.rope_theta, d)))
+            c, s = torch.cos(ang)[:, :, None, :], torch.sin(ang)[:, :, None, :]
+            rot = lambda t: torch.cat([t[..., :d // 2] * c - t[..., d // 2:] * s,
+                                       t[..., d // 2:] * c + t[..., :d // 2] * s], dim=-1)
+            qn, kn = rot(qn), rot(kn)
+        M = torch.tensor(np.stack([oracle.mask.explicit_mask(x.segments[b], S) for b in range(B)]))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qn.transpose(1, 2), kn.repeat_interleave(grp, dim=2).transpose(1, 2),
+            v.repeat_interleave(grp, dim=2).transpose(1, 2), attn_mask=M[:, None])
+        (o.transpose(1, 2) * torch.from_numpy(dout)).sum().backward()
+        g = oracle.backward.path_backward(x, dout)
+        for name, t in (("dq", q), ("dk", k), ("dv", v), ("dw_q", wq), ("dw_k", wk)):
+            if t is None:
+                assert g[name] is None, (rope, name)
+                continue
+            assert np.allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12), (rope, name)
+
+
+def pin_backward_invariants():
+    """Closed forms of the attention backward (no norm, no rotary):
+    - softmax rows sum to 1, so summed over keys dV_g equals the group's summed dO and
+      dZ sums to 0 in every row, which makes dK summed over keys 0;
+    - a row with one allowed key has a constant softmax, so its dq is 0;
+    - lse of an all-zero query row is log(number of allowed keys) (pair counts in closed form)."""
+    import oracle.backward
+    rng = np.random.default_rng(12)
+    table = np.array([[0, 5, C], [5, 12, G], [17, 9, F], [26, 4, C]])
+    S, Hq, Hkv, d = 30, 6, 2, 16
+    q = rng.standard_normal((1, S, Hq, d))
+    k = rng.standard_normal((1, S, Hkv, d))
+    v = rng.standard_normal((1, S, Hkv, d))
+    dout = rng.standard_normal((1, S, Hq, d))
+    M = oracle.mask.explicit_mask(table, S)
+    dq, dk, dv = oracle.backward.attention_backward(q, k, v, [M], dout)
+    for g in range(Hkv):
+        assert np.allclose(dk[0, :, g].sum(axis=0), 0.0, atol=1e-10), g
+        want = dout[0, :, 3 * g:3 * g + 3].sum(axis=(0, 1))
+        assert np.allclose(dv[0, :, g].sum(axis=0), want, atol=1e-10), g
+    assert np.allclose(dq[0, 0], 0.0, atol=1e-14)  # row 0 of a causal start sees key 0 only
+    q0 = q.copy()
+    q0[0, :, 0] = 0.0
+    lse = oracle.backward.attention_lse(q0, k, [M])
+    counts = np.array([(i + 1) if (i < 5 or i >= 26) else (17 if i < 17 else S) for i in range(S)])
+    assert np.allclose(lse[0, 0], np.log(counts), atol=1e-12)

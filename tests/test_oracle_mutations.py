@@ -5,6 +5,7 @@ sign, index or operand) and asserts that at least one of the listed pins fails."
 import numpy as np
 import pytest
 
+import oracle.backward
 import oracle.mask
 import oracle.masked_attention
 import oracle.norm
@@ -151,6 +152,62 @@ MUTATIONS = {
     "attn_transposed_scores": ([(oracle.masked_attention, "attention", _attn_transposed_scores)],
                                ["pin_attention_library"]),
 }
+
+
+# ---- backward (oracle/backward.py)
+def _bwd_variant(no_delta=False, overwrite_dv=False, unscaled_dk=False, untransposed_dz=False):
+    def attention_backward(q, k, v, masks, dout, scale=None, groups=None):
+        q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
+        B, S, Hq, d = q.shape
+        Hkv = k.shape[2]
+        group = Hq // Hkv
+        scale = (1.0 / np.sqrt(d)) if scale is None else scale
+        dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+        for b in range(B):
+            for g in range(Hkv):
+                K, V = k[b, :, g], v[b, :, g]
+                for h in range(g * group, (g + 1) * group):
+                    Q, dO = q[b, :, h], dout[b, :, h]
+                    Z = np.where(masks[b], Q @ K.T * scale, -np.inf)
+                    P = np.exp(Z - Z.max(-1, keepdims=True))
+                    P /= P.sum(-1, keepdims=True)
+                    dP = dO @ V.T
+                    dZ = P * dP if no_delta else P * (dP - np.sum(dO * (P @ V), -1, keepdims=True))
+                    if overwrite_dv:
+                        dv[b, :, g] = P.T @ dO
+                    else:
+                        dv[b, :, g] += P.T @ dO
+                    dq[b, :, h] = scale * dZ @ K
+                    dk[b, :, g] += (1.0 if unscaled_dk else scale) * ((dZ if untransposed_dz else dZ.T) @ Q)
+        return dq, dk, dv
+    return attention_backward
+
+
+def _rope_bwd_same_rotation(dy, angles):
+    return oracle.rope.apply_rope(dy, np.asarray(angles, dtype=np.float64))
+
+
+def _norm_bwd_first_term(x, weight, eps, dy):
+    x, dy, w = (np.asarray(a, dtype=np.float64) for a in (x, dy, weight))
+    r = 1.0 / np.sqrt(np.mean(x * x, -1, keepdims=True) + eps)
+    return r * dy * w, np.sum((dy * x * r).reshape(-1, x.shape[-1]), axis=0)
+
+
+_BWD_PINS = ["pin_backward_finite_differences", "pin_backward_autograd", "pin_backward_invariants"]
+MUTATIONS.update({
+    "bwd_softmax_without_delta": ([(oracle.backward, "attention_backward", _bwd_variant(no_delta=True))],
+                                  _BWD_PINS),
+    "bwd_dv_one_head_of_group": ([(oracle.backward, "attention_backward", _bwd_variant(overwrite_dv=True))],
+                                 _BWD_PINS),
+    "bwd_dk_without_scale": ([(oracle.backward, "attention_backward", _bwd_variant(unscaled_dk=True))],
+                             _BWD_PINS[:2]),
+    "bwd_dk_untransposed_dz": ([(oracle.backward, "attention_backward", _bwd_variant(untransposed_dz=True))],
+                               _BWD_PINS),
+    "bwd_rope_forward_rotation": ([(oracle.backward, "rope_backward", _rope_bwd_same_rotation)],
+                                  _BWD_PINS[:2]),
+    "bwd_norm_first_term_only": ([(oracle.backward, "rms_norm_backward", _norm_bwd_first_term)],
+                                 _BWD_PINS[:2]),
+})
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
