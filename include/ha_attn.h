@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 1
+#define HA_ABI_VERSION 2
 #define HA_MAX_SEGMENTS 64      /* segments per batch item */
 #define HA_MAX_SEQ_LEN (1 << 22)
 
@@ -173,6 +173,36 @@ ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const voi
 ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
                       const void* k, const void* v, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- training
+ * The pages train these models end to end (HiDream-O1 atlas page, "How it works";
+ * HunyuanImage 3.0 digest, training stages); the backward below is the derivative of the
+ * forward above (the pages print no backward formulas). bf16 only, n_q_heads / n_kv_heads
+ * in {1, 2, 4}; fp32 descriptors and groups of 8 return HA_ERR_UNSUPPORTED. */
+
+/* ha_attn_fwd, also writing the row log-sum-exp the backward needs: lse, DEVICE fp32
+ * [batch][n_q_heads][seq_len], the natural log of sum_j exp(scale q_i . k_j) over the keys
+ * row i attends (q, k after the prologue). Same workspace as ha_attn_fwd. */
+ha_status ha_attn_fwd_lse(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
+                          const void* k, const void* v, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes ha_attn_bwd needs: row limits, tile ranges, the rebuilt prologue
+ * outputs, per-row dout . out, fp32 gradients of the rotated q and k, and with RMSNorm
+ * per-token weight-gradient partials. */
+size_t ha_attn_bwd_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro);
+
+/* Gradients for the output gradient dout (same layout as out): dq, dk, dv with respect
+ * to ha_attn_fwd_lse's inputs q, k, v (same layouts; all bf16, DEVICE, 16-byte aligned);
+ * with RMSNorm in pro, dw_q and dw_k (DEVICE fp32 [head_dim], overwritten) with respect to
+ * the norm weights, else they must be NULL. out and lse are the forward's for the same
+ * desc, pro and inputs. desc->q_prescaled must be 0 (q is the path's input). The prologue
+ * is recomputed in the workspace (DEVICE, 256-byte aligned, >= ha_attn_bwd_workspace_bytes);
+ * nothing is allocated. Gradients accumulate in fp32; dq, dk, dv are rounded to bf16. */
+ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
+                      const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* dw_q, float* dw_k,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,10 +25,10 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = U.load_library()
     names = declared_functions()
-    assert len(names) == 10 and sorted(B.EXPORTS) == names
+    assert len(names) == 13 and sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
-    assert U.ha_abi_version() == 1
+    assert U.ha_abi_version() == 2
 
 
 def seg(rows, batch=1):
@@ -71,12 +71,16 @@ def test_bad_descriptor_rejected_everywhere(kw, status, text):
         lambda: U.ha_attn_fwd_planned(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
         lambda: U.ha_attn_fwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0),
         lambda: U.ha_qk_prologue(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, stream=0),
+        lambda: U.ha_attn_fwd_lse(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0),
+        lambda: U.ha_attn_bwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                              FAKE, 1 << 30, stream=0),
     ]
     for call in calls:
         with pytest.raises(U.HAError) as e:
             call()
         assert e.value.status == status and text in str(e.value), str(e.value)
     assert U.ha_attn_workspace_bytes(d) == 0
+    assert U.ha_attn_bwd_workspace_bytes(d) == 0
 
 
 def test_bad_pointers_and_workspace():
@@ -192,3 +196,47 @@ def test_workspace_layout():
     with_pro = U.ha_attn_workspace_bytes(d, U.PrologueDesc("none"))
     assert plain >= 2 * 4354 * 4 + 2 * 69 * 8
     assert with_pro - plain >= 2 * 4354 * 40 * 128 * 2
+
+
+def bf16_desc(**kw):
+    base = dict(batch=1, seq_len=80, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16",
+                segments=seg([[0, 16, 0], [16, 64, 1]]))
+    base.update(kw)
+    return U.AttnDesc(**base)
+
+
+def test_training_entry_points_reject_before_launch():
+    F = FAKE
+    bwd = lambda d, p=None, dwq=None, dwk=None, ws=F, n=1 << 30, lse=F: U.ha_attn_bwd(
+        d, p, F, F, F, F, lse, F, F, F, F, dwq, dwk, ws, n, stream=0)
+    cases = [
+        # fp32 tensors and groups of 8 query heads per KV head have no training kernels
+        (lambda: U.ha_attn_fwd_lse(desc(), None, F, F, F, F, F, F, 1 << 30, stream=0), B.HA_ERR_UNSUPPORTED, "bf16"),
+        (lambda: bwd(desc()), B.HA_ERR_UNSUPPORTED, "bf16"),
+        (lambda: bwd(bf16_desc(n_q_heads=16)), B.HA_ERR_UNSUPPORTED, "1, 2, 4"),
+        (lambda: U.ha_attn_fwd_lse(bf16_desc(), None, F, F, F, F, None, F, 1 << 30, stream=0),
+         B.HA_ERR_INVALID_ARG, "lse"),
+        (lambda: bwd(bf16_desc(), lse=None), B.HA_ERR_INVALID_ARG, "lse"),
+        (lambda: bwd(bf16_desc(q_prescaled=1)), B.HA_ERR_INVALID_ARG, "q_prescaled"),
+        # weight gradients exactly when the prologue normalises
+        (lambda: bwd(bf16_desc(), dwq=F, dwk=F), B.HA_ERR_INVALID_ARG, "dw_q"),
+        (lambda: bwd(bf16_desc(), U.PrologueDesc("none", q_norm_weight=F, k_norm_weight=F)),
+         B.HA_ERR_INVALID_ARG, "dw_q"),
+        (lambda: bwd(bf16_desc(), ws=None), B.HA_ERR_WORKSPACE, "NULL"),
+        (lambda: bwd(bf16_desc(), n=U.ha_attn_bwd_workspace_bytes(bf16_desc()) - 1), B.HA_ERR_WORKSPACE, "needs"),
+    ]
+    for call, status, text in cases:
+        with pytest.raises(U.HAError) as e:
+            call()
+        assert e.value.status == status and text in str(e.value), str(e.value)
+
+
+def test_backward_workspace_layout():
+    d = bf16_desc(batch=2, seq_len=4354, n_q_heads=32, n_kv_heads=8,
+                  segments=seg([[0, 258, 0], [258, 4096, 1]], 2))
+    plain = U.ha_attn_bwd_workspace_bytes(d)
+    normed = U.ha_attn_bwd_workspace_bytes(d, U.PrologueDesc("none", q_norm_weight=FAKE, k_norm_weight=FAKE))
+    tokens = 2 * 4354
+    # bf16 rebuilt q, k + fp32 gradients of both + per-row delta
+    assert plain >= tokens * 40 * 128 * (2 + 4) + tokens * 32 * 4
+    assert normed - plain >= 2 * tokens * 128 * 4

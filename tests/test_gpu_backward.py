@@ -1,0 +1,172 @@
+"""Training path against the oracle's gradients, through the C ABI.
+
+ha_attn_fwd_lse, then ha_attn_bwd with a seeded bf16 output gradient; the oracle's
+path_backward (fp64; pinned by finite differences, torch autograd and closed forms) is the
+reference for dq, dk, dv and the norm-weight gradients, attention_lse for the lse.
+
+Tolerance. Every product runs on bf16 operands (q', k, v, dO, and P or dZ rounded to bf16)
+with fp32 accumulation, and dq, dk, dv are rounded to bf16: a gradient row (one token and
+head over the head dim) is a sum of terms carrying two to four bf16 roundings (relative
+2^-9 each), so its rms error is a few times 2^-9 of the row's own size. Row sizes differ by
+an order of magnitude (a causal row near the start of the sequence, with few keys, has a
+far larger dq than a full row), so the bound is per row. A row's rounding error follows the
+size of its terms (P (dP - delta) k), not of their sum, which cancels in some rows (and is
+exactly zero for dq of a row that sees one key), so each row is measured against the larger
+of its own rms and ROW_FLOOR * rms of the whole tensor. The bulk of the rows (99%) must
+stay within GRAD_ROW_BULK (a few roundings); any row within GRAD_ROW, which leaves room for
+terms up to ~10x the row's floored size (3 roundings x 2^-9 x 10 ~ 6%); and mean |err| <=
+GRAD_MEAN * rms over the tensor. A wrong tile or mask leaves errors the size of the row
+itself. The norm-weight gradients are one row each. lse is the log of a sum of exponentials of
+bf16-operand scores: |err| <= LSE_ABS."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import desc_for, f64, prologue_for, require_gpu
+from unified_text_pixel_amd import binding as B
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+C, F, G = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA
+GRAD_ROW, GRAD_ROW_BULK, GRAD_MEAN, ROW_FLOOR, LSE_ABS = 5e-2, 1e-2, 1e-2, 0.5, 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def small(segs, hq=8, hkv=2, d=128, rope="mrope", norm=True, batch=2, theta=5e6, seed=31):
+    sections = (24, 20, 20) if d == 128 else (12, 10, 10)
+    return W.Workload(name="small", description="", batch=batch, segments=tuple(segs),
+                      n_q_heads=hq, n_kv_heads=hkv, head_dim=d, dtype="bf16", rope=rope,
+                      rope_theta=theta, mrope_sections=sections, qk_norm=norm, norm_eps=1e-6,
+                      seed=seed)
+
+
+SMALL = {
+    "hd_small": small([W.Segment(C, 70), W.Segment(F, 256, (16, 16))]),
+    "edit_small": small([W.Segment(C, 40), W.Segment(F, 100, (10, 10)), W.Segment(C, 81, (9, 9))]),
+    "gca_small": small([W.Segment(C, 33), W.Segment(G, 64, (8, 8)), W.Segment(G, 49, (7, 7)),
+                        W.Segment(C, 17), W.Segment(G, 100, (10, 10)), W.Segment(C, 5)],
+                       rope="2d", norm=False, theta=1e4),
+    "mha_g1": small([W.Segment(C, 50), W.Segment(F, 150)], hq=2, hkv=2, rope="1d"),
+    "gqa_g2": small([W.Segment(C, 50), W.Segment(F, 150)], hq=4, hkv=2, rope="1d"),
+    "d64": small([W.Segment(C, 45), W.Segment(G, 81, (9, 9)), W.Segment(C, 3)], d=64),
+    "d64_g1": small([W.Segment(F, 70), W.Segment(C, 60)], hq=2, hkv=2, d=64, rope="none"),
+    "d64_g2": small([W.Segment(C, 90), W.Segment(F, 49, (7, 7))], hq=4, hkv=2, d=64, norm=False),
+    "one_token": small([W.Segment(C, 1)], batch=3),
+    "all_causal": small([W.Segment(C, 300)], rope="1d"),
+    "all_full": small([W.Segment(F, 200)], rope="2d", theta=1e4),
+    "no_prologue": small([W.Segment(C, 37), W.Segment(F, 64, (8, 8))], rope="none", norm=False),
+    "rows_before_keys_of_block": small([W.Segment(C, 3), W.Segment(F, 130)], hq=4, hkv=1),
+}
+
+
+def output_grad(w, seed=77):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((w.batch, w.seq_len, w.n_q_heads, w.head_dim), dtype=np.float32)
+    return W.bf16_bits_to_f32(W.f32_to_bf16_bits(g)).reshape(g.shape)
+
+
+def run_train(x, dout_np):
+    """Forward with lse and backward on the GPU; returns host float64 arrays."""
+    w = x.workload
+    dev = to_device(x)
+    desc = desc_for(w, x.segments)
+    pro = prologue_for(w, dev)
+    ws = torch.empty(max(256, B.ha_attn_workspace_bytes(desc, pro),
+                         B.ha_attn_bwd_workspace_bytes(desc, pro)), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((w.batch, w.n_q_heads, w.seq_len), dtype=torch.float32, device="cuda")
+    B.ha_attn_fwd_lse(desc, pro, dev["q"], dev["k"], dev["v"], out, lse, ws)
+    dout = torch.from_numpy(dout_np).to(torch.bfloat16).cuda()
+    dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
+    norm = w.qk_norm
+    dwq = torch.full((w.head_dim,), float("nan"), device="cuda") if norm else None
+    dwk = torch.full((w.head_dim,), float("nan"), device="cuda") if norm else None
+    B.ha_attn_bwd(desc, pro, dev["q"], dev["k"], dev["v"], out, lse, dout, dq, dk, dv, dwq, dwk, ws)
+    torch.cuda.synchronize()
+    res = {"out": f64(out), "lse": f64(lse), "dq": f64(dq), "dk": f64(dk), "dv": f64(dv)}
+    if norm:
+        res["dw_q"], res["dw_k"] = f64(dwq), f64(dwk)
+    return res
+
+
+def check(name, got, want):
+    assert np.isfinite(got).all(), f"{name}: non-finite"
+    err = got - want
+    rms = float(np.sqrt(np.mean(want * want)))
+    mean = float(np.abs(err).mean())
+    row_ref = np.sqrt(np.mean(want * want, axis=-1))
+    row_err = np.sqrt(np.mean(err * err, axis=-1))
+    row_rel = row_err / np.maximum(row_ref, ROW_FLOOR * rms + 1e-30)
+    worst = float(row_rel.max())
+    bulk = float(np.quantile(row_rel, 0.99))
+    print(f"{name}: rms {rms:.3e}  row rms(err)/rms(ref): worst {worst:.3e} p99 {bulk:.3e} "
+          f"median {float(np.median(row_rel)):.3e}  mean|err|/rms {mean / max(rms, 1e-30):.3e}", flush=True)
+    if rms == 0.0:
+        # e.g. a single token: the exact gradients are zero, and what the kernels leave is
+        # fp32 residue (dP = dO.v and delta = dO.out summed in different orders), ~1e-7 per
+        # term, against gradients of size ~0.1 to 10 elsewhere
+        assert float(np.abs(err).max()) <= 1e-4, name
+        return
+    assert worst <= GRAD_ROW and bulk <= GRAD_ROW_BULK and mean <= GRAD_MEAN * rms, (name, worst, bulk, mean)
+
+
+def check_lse(got, want):
+    err = float(np.abs(got - want).max())
+    print(f"lse: max|err| {err:.3e}", flush=True)
+    assert err <= LSE_ABS, err
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_backward_small_layouts(name):
+    w = SMALL[name]
+    print(f"case {name}: S={w.seq_len} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim}", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w)
+    got = run_train(x, dout)
+    masks = [oracle.explicit_mask(x.segments[b], w.seq_len) for b in range(w.batch)]
+    q_rot, k_rot = oracle.prologue(x)
+    check_lse(got["lse"], oracle.attention_lse(q_rot, k_rot, masks))
+    want = oracle.path_backward(x, dout)
+    for t in ("dq", "dk", "dv"):
+        check(f"{name} {t}", got[t], want[t])
+    if w.qk_norm:
+        for t in ("dw_q", "dw_k"):
+            check(f"{name} {t}", got[t], want[t])
+
+
+def test_backward_hd1024_full():
+    """The 1024^2 HiDream layout at full size (both batch items, every head)."""
+    w = W.get_config("hd1024")
+    print("case hd1024: full compare", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w, seed=78)
+    got = run_train(x, dout)
+    want = oracle.path_backward(x, dout)
+    for t in ("dq", "dk", "dv", "dw_q", "dw_k"):
+        check(f"hd1024 {t}", got[t], want[t])
+
+
+def test_backward_hd2048_one_group():
+    """The 2048^2 layout in the benchmark's launch configuration; the oracle computes KV
+    group 3 of batch item 1 (its 4 query heads' dq, its dk and dv)."""
+    w = W.get_config("hd2048")
+    print("case hd2048: group 3 of item 1", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w, seed=79)
+    got = run_train(x, dout)
+    one = dataclasses.replace(x, workload=w.replace(batch=1), q=x.q[1:], k=x.k[1:], v=x.v[1:],
+                              positions=x.positions[1:], segments=x.segments[1:])
+    want = oracle.path_backward(one, dout[1:], groups=[3])
+    heads = slice(12, 16)
+    check("hd2048 dq", got["dq"][1, :, heads], want["dq"][0, :, heads])
+    check("hd2048 dk", got["dk"][1, :, 3], want["dk"][0, :, 3])
+    check("hd2048 dv", got["dv"][1, :, 3], want["dv"][0, :, 3])

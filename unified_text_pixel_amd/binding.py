@@ -27,7 +27,8 @@ ROPE_KINDS = {"none": HA_ROPE_NONE, "1d": HA_ROPE_1D, "2d": HA_ROPE_2D, "mrope":
 # Every function include/ha_attn.h declares.
 EXPORTS = ("ha_abi_version", "ha_last_error", "ha_rope_table_fill", "ha_q_prescale",
            "ha_tile_shape", "ha_classify_tiles", "ha_qk_prologue", "ha_attn_workspace_bytes",
-           "ha_attn_fwd_planned", "ha_attn_fwd")
+           "ha_attn_fwd_planned", "ha_attn_fwd", "ha_attn_fwd_lse", "ha_attn_bwd_workspace_bytes",
+           "ha_attn_bwd")
 
 
 class HAError(RuntimeError):
@@ -82,6 +83,9 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
         "ha_attn_workspace_bytes": ([D, PD], SZ),
         "ha_attn_fwd_planned": ([D, P, P, P, P, P, P, P], ctypes.c_int),
         "ha_attn_fwd": ([D, PD, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "ha_attn_fwd_lse": ([D, PD, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "ha_attn_bwd_workspace_bytes": ([D, PD], SZ),
+        "ha_attn_bwd": ([D, PD, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -208,3 +212,28 @@ def ha_attn_fwd(desc: AttnDesc, pro: Optional[PrologueDesc], q, k, v, out, works
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().ha_attn_fwd(_d(desc), _pd(pro), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                       _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def _nbytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return int(workspace_bytes)
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def ha_attn_fwd_lse(desc: AttnDesc, pro: Optional[PrologueDesc], q, k, v, out, lse, workspace,
+                    workspace_bytes: Optional[int] = None, stream=None):
+    _check(load_library().ha_attn_fwd_lse(_d(desc), _pd(pro), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                          _ptr(lse), _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                          _stream(stream)))
+
+
+def ha_attn_bwd_workspace_bytes(desc: AttnDesc, pro: Optional[PrologueDesc] = None) -> int:
+    return load_library().ha_attn_bwd_workspace_bytes(_d(desc), _pd(pro))
+
+
+def ha_attn_bwd(desc: AttnDesc, pro: Optional[PrologueDesc], q, k, v, out, lse, dout, dq, dk, dv,
+                dw_q, dw_k, workspace, workspace_bytes: Optional[int] = None, stream=None):
+    _check(load_library().ha_attn_bwd(_d(desc), _pd(pro), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                      _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw_q),
+                                      _ptr(dw_k), _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                      _stream(stream)))

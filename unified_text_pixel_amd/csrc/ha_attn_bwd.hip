@@ -1,0 +1,512 @@
+// Backward of the hybrid-mask GQA attention for gfx950 (CDNA4).
+//
+// For a loss with output gradient dO (row i attends the key prefix [0, lim(i)); query head
+// h shares KV head g; Z_ij = scale q_i . k_j; P = softmax of Z over the row's keys):
+//   dV_j  = sum over the heads h of g and rows i of  P_ij dO_i        dP_ij = dO_i . v_j
+//   dZ_ij = P_ij (dP_ij - delta_i),   delta_i = dO_i . O_i
+//   dQ_i  = scale sum_j dZ_ij k_j,    dK_j = scale sum over h and i of dZ_ij q_i
+// This is the derivative of the forward in ha_attn_fwd.hip: the pages train the models
+// end to end (HiDream-O1 atlas page, "How it works"; HunyuanImage 3.0 digest, training
+// stages) but print no backward. P is rebuilt from the forward's row log-sum-exp,
+// P_ij = exp(Z_ij - lse_i); q comes in as q' = scale log2(e) q (the prologue's prescaled
+// output), so q' . k is Z in log2 units and P = exp2(q' . k - log2(e) lse).
+//
+// bwd_dkdv: one workgroup per (batch, KV head, block of 256/G keys). Wave w serves query
+//   head g*G + w%G and keys 32*(w/G) .. +32 of the block. Per step of 32 query rows the
+//   q' and dO rows of all G heads are copied into LDS (global_load_lds, double-buffered).
+//   In the orientation S = Q' K^T (v_mfma_f32_32x32x16_bf16, A = q' rows, B = K^T, both
+//   from LDS) a lane holds one key and 16 of the 32 rows, so P and dZ rounded to bf16 are
+//   already the A operand of dV += P^T dO and dK += dZ^T Q', whose B operands are the dO
+//   and q' rows gathered in the same row order by ds_read_b64_tr_b16. A row's lse, delta
+//   and limit come from the lane that loaded them (ds_bpermute). At the end the G heads'
+//   partial sums meet in LDS.
+// bwd_dq: the forward's shape: one workgroup per (batch, KV head, query block), one lane
+//   per query row. Per 64-key tile S^T = K Q'^T and dP^T = V dO^T (A from LDS, B = the
+//   row's q' and dO held in registers); dZ^T, rounded to bf16, is the B operand of
+//   dQ^T += K^T dZ^T (A = K^T gathered from LDS by ds_read_b64_tr_b16).
+// bwd_delta: delta = rowsum(dO * O) in fp32.
+//
+// LDS tiles are row-major with 16-byte chunks XOR-swizzled by (row mod chunks per row);
+// a step tile of q' or dO keeps the G heads of one row side by side.
+#include <type_traits>
+
+#include "ha_internal.h"
+
+namespace ha {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int BK = kBlockK;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.693147180559945309417f;
+
+__device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float bpermute(int src_lane, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src_lane, __builtin_bit_cast(int, x)));
+}
+
+// Copies rows [row0, row0 + rows) of a row-major global tensor (row stride gstride bytes,
+// rows clamped to [0, rmax]) into LDS, ROWB bytes per row made of segments of D elements
+// (one per head), each swizzled by the row within the tile. 1 KB per DMA instruction;
+// instruction ins is issued by wave ins mod 8 (wave is wave-uniform).
+template <int D, int ROWB, int NINS>
+__device__ __attribute__((always_inline)) inline void dma_rows(const char* gbase, int64_t gstride, int row0, int rmax, char* lds, int wave,
+                                int lane) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int j = 0; j < (NINS + 7) / 8; ++j) {
+    const int ins = wave + 8 * j;  // a run-time index keeps the LDS address out of constant folding
+    if (NINS % 8 != 0 && ins >= NINS) continue;
+    const int off = ins * 1024 + 16 * lane;
+    const int rho = off / ROWB, rem = off % ROWB;
+    const int seg = rem / (2 * D), pc = (rem % (2 * D)) / 16;
+    const int lc = pc ^ (rho & (CPR - 1));
+    const int r = min(max(row0 + rho, 0), rmax);
+    const char* src = gbase + r * gstride + seg * (2 * D) + lc * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + ins * 1024), 16, 0, 0);
+  }
+}
+
+// (batch * KV heads) pair and block slot of workgroup x: XCD-aware when the pairs split
+// evenly over the 8 XCDs (workgroups go round-robin to XCDs), so each XCD's L2 holds the
+// tensors of its own pairs.
+__device__ inline void pair_slot(int x, int nbg, int nblocks, int* bg, int* slot) {
+  if (nbg % 8 == 0) {
+    const int xcd = x % 8, s = x / 8;
+    *bg = xcd + 8 * (s / nblocks);
+    *slot = s % nblocks;
+  } else {
+    *bg = x / nblocks;
+    *slot = x % nblocks;
+  }
+}
+
+// ====================================================================== delta
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta(const __bf16* out, const __bf16* dout, float* delta, int B, int S,
+                                                 int Hq) {
+  constexpr int LPR = D / 8;  // lanes per (token, head) row, 8 elements each
+  const int64_t n = (int64_t)B * S * Hq;
+  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int c = threadIdx.x % LPR;
+  float s = 0.f;
+  if (r < n) {
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + r * D + 8 * c);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dout + r * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += static_cast<float>(o[e]) * static_cast<float>(g[e]);
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (r < n && c == 0) {
+    const int h = (int)(r % Hq);
+    const int64_t bi = r / Hq;
+    delta[((bi / S) * Hq + h) * S + bi % S] = s;
+  }
+}
+
+// ====================================================================== dK, dV
+template <int D, int G>
+struct CfgKV {
+  static constexpr int NS = 8 / G;                // 32-key slices per work item
+  static constexpr int KB = 32 * NS;              // keys per work item
+  static constexpr int CPR = D / 8;               // 16-byte chunks per head row
+  static constexpr int QROWB = G * D * 2;         // one step row: the G heads' q' (or dO)
+  static constexpr int QBYTES = 32 * QROWB;       // one step tile (32 rows)
+  static constexpr int KVBYTES = KB * D * 2;      // the item's K (or V) rows
+  static constexpr int SUB = 8 / G;               // 32-row steps per query block
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
+  using C = CfgKV<D, G>;
+  __shared__ __attribute__((aligned(1024))) char kt[C::KVBYTES];
+  __shared__ __attribute__((aligned(1024))) char vt[C::KVBYTES];
+  __shared__ __attribute__((aligned(1024))) char q0[C::QBYTES];
+  __shared__ __attribute__((aligned(1024))) char q1[C::QBYTES];
+  __shared__ __attribute__((aligned(1024))) char o0[C::QBYTES];
+  __shared__ __attribute__((aligned(1024))) char o1[C::QBYTES];
+
+  const int S = a.S, nq = a.nq;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave % G, ksl = wave / G;
+  const int hi = lane >> 5, ln = lane & 31;
+  const int nkb = (S + C::KB - 1) / C::KB;
+  int bg, kbk;
+  pair_slot(blockIdx.x, a.B * a.Hkv, nkb, &bg, &kbk);
+  const int b = bg / a.Hkv, g = bg % a.Hkv, h = g * G + hg;
+  const int k0 = kbk * C::KB;
+  const int key = k0 + 32 * ksl + ln;  // this lane's key (lanes l and l + 32 share it)
+  const int BQ = 32 * C::SUB;          // rows of a forward query block
+  const int qrow0 = S - nq * BQ;       // first row of query block 0 (end-aligned blocks)
+
+  // the item's K and V rows
+  const int64_t kvstride = (int64_t)a.Hkv * D * 2;
+  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * S * a.Hkv + g) * D * 2;
+  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)b * S * a.Hkv + g) * D * 2;
+  dma_rows<D, 2 * D, C::KVBYTES / 1024>(kbase, kvstride, k0, S - 1, kt, wave, lane);
+  dma_rows<D, 2 * D, C::KVBYTES / 1024>(vbase, kvstride, k0, S - 1, vt, wave, lane);
+
+  // step s = 32 rows starting at qrow0 + 32 s; active when its query block attends a key
+  // >= k0 (then it attends k0: rows see prefixes) and some row is >= 0
+  const int nsteps = nq * C::SUB;
+  auto next_step = [&](int s) __attribute__((always_inline)) {
+    for (++s; s < nsteps; ++s) {
+      if (qrow0 + 32 * s + 31 < 0) continue;
+      const int qb = s / C::SUB;
+      if (a.ranges[((int64_t)b * nq + qb) * 2 + 1] * BK > k0) return s;
+      s = (qb + 1) * C::SUB - 1;
+    }
+    return -1;
+  };
+
+  const int64_t qstride = (int64_t)a.Hq * D * 2;
+  const char* qbase = static_cast<const char*>(a.q) + ((int64_t)b * S * a.Hq + g * G) * D * 2;
+  const char* obase = static_cast<const char*>(a.dout) + ((int64_t)b * S * a.Hq + g * G) * D * 2;
+  const float* lse_h = a.lse + ((int64_t)b * a.Hq + h) * S;
+  const float* del_h = a.delta + ((int64_t)b * a.Hq + h) * S;
+  const int32_t* lim_b = a.row_limit + (int64_t)b * S;
+  // step s into a tile pair; the lane's row (ln) values into registers: log2(e) lse,
+  // delta and the row's key limit (0 for rows before the sequence, which see no key)
+  auto fetch = [&](int s, char* qd, char* od, float& lr, float& dr, int& mr) __attribute__((always_inline)) {
+    const int r0 = qrow0 + 32 * s;
+    dma_rows<D, C::QROWB, C::QBYTES / 1024>(qbase, qstride, r0, S - 1, qd, wave, lane);
+    dma_rows<D, C::QROWB, C::QBYTES / 1024>(obase, qstride, r0, S - 1, od, wave, lane);
+    const int i = r0 + ln;
+    const int ic = max(i, 0);
+    lr = lse_h[ic] * kLog2e;
+    dr = del_h[ic];
+    mr = i >= 0 ? lim_b[ic] : 0;
+  };
+
+  // A/B operand reads of rows (q' or dO row ln, or K/V row 32 ksl + ln): chunk 2kk + hi of
+  // the row sits at (2kk) ^ kx
+  const int kx = hi ^ (ln & (C::CPR - 1));
+  // transposing reads: lane t of 16-lane group G16 points at row 16KS + 8rr + 4(G16 >> 1)
+  // + t/4 and dims 32mt + 16(G16 & 1) + 4(t & 3)
+  const int g16 = lane >> 4, t16 = lane & 15;
+  const int vrow = 4 * (g16 >> 1) + (t16 >> 2);
+  const int vclow = 2 * (g16 & 1) + ((t16 & 3) >> 1);
+  const int vhalf = 8 * (t16 & 1);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16{};
+
+  auto compute = [&](const char* qc, const char* oc, float lr, float dr, int mr) __attribute__((always_inline)) {
+    // S = Q' K^T and dP = dO V^T: rows x keys, lane = key, register r = row 8(r/4) + 4hi + r%4
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    const char* qrow = qc + (ln * G + hg) * (2 * D);
+    const char* orow = oc + (ln * G + hg) * (2 * D);
+    const char* krow = kt + (32 * ksl + ln) * (2 * D);
+    const char* vrowp = vt + (32 * ksl + ln) * (2 * D);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int off = ((2 * kk) ^ kx) * 16;
+      sacc = mfma(*reinterpret_cast<const bf16x8*>(qrow + off), *reinterpret_cast<const bf16x8*>(krow + off), sacc);
+      pacc = mfma(*reinterpret_cast<const bf16x8*>(orow + off), *reinterpret_cast<const bf16x8*>(vrowp + off), pacc);
+    }
+    // P = exp2(S - log2(e) lse) on allowed (row, key) pairs, dZ = P (dP - delta); both to
+    // bf16 with rows 16KS .. 16KS + 15 in register order (the A-operand k order)
+    bf16x8 pa[2], za[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int src = 8 * (r >> 2) + 4 * hi + (r & 3);
+      const float l2 = bpermute(src, lr);
+      const float de = bpermute(src, dr);
+      const int lim = __builtin_bit_cast(int, bpermute(src, __builtin_bit_cast(float, mr)));
+      const float p = key < lim ? __builtin_amdgcn_exp2f(sacc[r] - l2) : 0.f;
+      pa[r >> 3][r & 7] = static_cast<__bf16>(p);
+      za[r >> 3][r & 7] = static_cast<__bf16>(p * (pacc[r] - de));
+    }
+    // dV += P^T dO, dK += dZ^T Q' (B: dO / q' rows of this head gathered per dims 32mt..)
+#pragma unroll
+    for (int KS = 0; KS < 2; ++KS) {
+      const int rl = 16 * KS + vrow, ru = rl + 8;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const int cl = (((4 * mt + vclow) ^ (rl & (C::CPR - 1))) * 16) + vhalf;
+        const int cu = (((4 * mt + vclow) ^ (ru & (C::CPR - 1))) * 16) + vhalf;
+        const char* ol = oc + (rl * G + hg) * (2 * D) + cl;
+        const char* ou = oc + (ru * G + hg) * (2 * D) + cu;
+        const bf16x4 dol = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ol);
+        const bf16x4 dou = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ou);
+        dv[mt] = mfma(pa[KS], __builtin_shufflevector(dol, dou, 0, 1, 2, 3, 4, 5, 6, 7), dv[mt]);
+        const char* ql = qc + (rl * G + hg) * (2 * D) + cl;
+        const char* qu = qc + (ru * G + hg) * (2 * D) + cu;
+        const bf16x4 qvl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ql);
+        const bf16x4 qvu = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)qu);
+        dk[mt] = mfma(za[KS], __builtin_shufflevector(qvl, qvu, 0, 1, 2, 3, 4, 5, 6, 7), dk[mt]);
+      }
+    }
+  };
+
+  // two steps per trip, tile pair (q0, o0) then (q1, o1); every step first lands its own
+  // tiles (wait + barrier, which also retires every wave's reads of the pair it refills)
+  float la = 0.f, da = 0.f, lb = 0.f, db = 0.f;
+  int ma = 0, mb = 0;
+  int s = next_step(-1);
+  if (s >= 0) fetch(s, q0, o0, la, da, ma);
+  while (s >= 0) {
+    const int s1 = next_step(s);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (s1 >= 0) fetch(s1, q1, o1, lb, db, mb);
+    compute(q0, o0, la, da, ma);
+    if (s1 < 0) break;
+    const int s2 = next_step(s1);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (s2 >= 0) fetch(s2, q0, o0, la, da, ma);
+    compute(q1, o1, lb, db, mb);
+    s = s2;
+  }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K/V DMA of an item with no step
+
+  // dK for the rotated k: scale * sum dZ q = ln(2) * sum dZ q' (q' = scale log2(e) q)
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dk[mt] *= kLn2;
+
+  // sum the G heads' partials (waves ksl*G .. +G) through LDS, 8 registers per lane per
+  // round; wave hg == 0 of each slice stores. Element (r, lane) of dv[mt] / dk[mt] is key
+  // k0 + 32 ksl + 8(r/4) + 4hi + r%4, dim 32 mt + ln.
+  float* red = reinterpret_cast<float*>(C::QBYTES >= 16384 ? q0 : kt);
+  __bf16* dvo = static_cast<__bf16*>(a.dv) + ((int64_t)b * S * a.Hkv + g) * D;
+  float* dko = a.dk + ((int64_t)b * S * a.Hkv + g) * D;
+  auto emit = [&](int which, int mt, int half, const float (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 8 * half + e;
+      const int kj = k0 + 32 * ksl + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (kj >= S) continue;
+      const int64_t at = (int64_t)kj * a.Hkv * D + 32 * mt + ln;
+      if (which == 0)
+        dvo[at] = static_cast<__bf16>(x[e]);
+      else
+        dko[at] = x[e];
+    }
+  };
+#pragma unroll
+  for (int which = 0; which < 2; ++which)
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x16& acc = which == 0 ? dv[mt] : dk[mt];
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = acc[8 * half + e];
+        if constexpr (G > 1) {
+          __syncthreads();  // the previous round's (or the last step's) reads are done
+          f32x4* w = reinterpret_cast<f32x4*>(red + (wave * 64 + lane) * 8);
+          w[0] = f32x4{x[0], x[1], x[2], x[3]};
+          w[1] = f32x4{x[4], x[5], x[6], x[7]};
+          __syncthreads();
+          if (hg == 0) {
+#pragma unroll
+            for (int o = 1; o < G; ++o) {
+              const f32x4* rd = reinterpret_cast<const f32x4*>(red + ((wave + o) * 64 + lane) * 8);
+              const f32x4 u = rd[0], v = rd[1];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                x[e] += u[e];
+                x[4 + e] += v[e];
+              }
+            }
+            emit(which, mt, half, x);
+          }
+        } else {
+          emit(which, mt, half, x);
+        }
+      }
+}
+
+// ====================================================================== dQ
+template <int D, int G>
+struct CfgQ {
+  static constexpr int TSUB = 8 / G;
+  static constexpr int BQ = 32 * TSUB;
+  static constexpr int CPR = D / 8;
+  static constexpr int TBYTES = BK * D * 2;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
+  using C = CfgQ<D, G>;
+  __shared__ __attribute__((aligned(1024))) char k0[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[C::TBYTES];
+
+  const int S = a.S, nq = a.nq;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave % G, tsub = wave / G;
+  const int hi = lane >> 5, ln = lane & 31;
+  int bg, slot;
+  pair_slot(blockIdx.x, a.B * a.Hkv, nq, &bg, &slot);
+  const int b = bg / a.Hkv, g = bg % a.Hkv, h = g * G + hg;
+  const int qb = nq - 1 - slot;  // query blocks from the last (full rows) to the first
+  const int i = S - (nq - qb) * C::BQ + tsub * 32 + ln;
+  const bool row_ok = i >= 0;
+  const int ic = row_ok ? i : 0;
+  const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : 0;
+  const int kend = a.ranges[((int64_t)b * nq + qb) * 2 + 1];
+
+  const int64_t kvstride = (int64_t)a.Hkv * D * 2;
+  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * S * a.Hkv + g) * D * 2;
+  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)b * S * a.Hkv + g) * D * 2;
+  dma_rows<D, 2 * D, C::TBYTES / 1024>(kbase, kvstride, 0, S - 1, k0, wave, lane);
+  dma_rows<D, 2 * D, C::TBYTES / 1024>(vbase, kvstride, 0, S - 1, v0, wave, lane);
+
+  // the row's q' and dO as B operands (dims 16kk + 8hi .. +8), its log2(e) lse and delta
+  bf16x8 qf[D / 16], of[D / 16];
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + (((int64_t)b * S + ic) * a.Hq + h) * D;
+  const __bf16* op = static_cast<const __bf16*>(a.dout) + (((int64_t)b * S + ic) * a.Hq + h) * D;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hi);
+    of[kk] = *reinterpret_cast<const bf16x8*>(op + 16 * kk + 8 * hi);
+  }
+  const float l2 = a.lse[((int64_t)b * a.Hq + h) * S + ic] * kLog2e;
+  const float de = a.delta[((int64_t)b * a.Hq + h) * S + ic];
+
+  const int krow = ln;
+  const int kx = hi ^ (krow & (C::CPR - 1));
+  const int g16 = lane >> 4, t16 = lane & 15;
+  const int vrow = 4 * (g16 >> 1) + (t16 >> 2);
+  const int vclow = 2 * (g16 & 1) + ((t16 & 3) >> 1);
+  const int vhalf = 8 * (t16 & 1);
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
+
+  // X^T (keys x rows) = T B^T for the 64 rows of tile buffer tb and the row fragments bf
+  auto rows_times = [&](const char* tb, const bf16x8 (&bf)[D / 16], f32x16 (&s)[2]) __attribute__((always_inline)) {
+    s[0] = s[1] = f32x16{};
+    const char* r0 = tb + krow * (2 * D);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int off = ((2 * kk) ^ kx) * 16;
+      s[0] = mfma(*reinterpret_cast<const bf16x8*>(r0 + off), bf[kk], s[0]);
+      s[1] = mfma(*reinterpret_cast<const bf16x8*>(r0 + 32 * 2 * D + off), bf[kk], s[1]);
+    }
+  };
+
+  auto step = [&](auto par_tag, int t) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_tag)::value;
+    const char* const kc = PAR ? k1 : k0;
+    const char* const vc = PAR ? v1 : v0;
+    char* const kn = PAR ? k0 : k1;
+    char* const vn = PAR ? v0 : v1;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < kend) {
+      dma_rows<D, 2 * D, C::TBYTES / 1024>(kbase, kvstride, (t + 1) * BK, S - 1, kn, wave, lane);
+      dma_rows<D, 2 * D, C::TBYTES / 1024>(vbase, kvstride, (t + 1) * BK, S - 1, vn, wave, lane);
+    }
+    f32x16 st[2], pt[2];
+    rows_times(kc, qf, st);  // S^T = K Q'^T
+    rows_times(vc, of, pt);  // dP^T = V dO^T
+    // dZ^T = P^T (dP^T - delta) on allowed keys, to bf16 in B-operand order (keys
+    // 16KS .. 16KS + 15 of the tile in register order)
+    bf16x8 zf[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float p = key < lim ? __builtin_amdgcn_exp2f(st[kt][r] - l2) : 0.f;
+        zf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pt[kt][r] - de));
+      }
+    // dQ^T += K^T dZ^T: A = K^T (dims 32mt .., keys of step KS) gathered from LDS
+#pragma unroll
+    for (int KS = 0; KS < BK / 16; ++KS) {
+      const int rl = 16 * KS + vrow, ru = rl + 8;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const char* pl = kc + rl * (2 * D) + (((4 * mt + vclow) ^ (rl & (C::CPR - 1))) * 16) + vhalf;
+        const char* pu = kc + ru * (2 * D) + (((4 * mt + vclow) ^ (ru & (C::CPR - 1))) * 16) + vhalf;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pl);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pu);
+        dq[mt] = mfma(__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7), zf[KS], dq[mt]);
+      }
+    }
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 1 < kend; t += 2) {
+    step(P0{}, t);
+    step(P1{}, t + 1);
+  }
+  if (t < kend) step(P0{}, t);
+
+  // dQ for the rotated q: scale * sum dZ k; element (mt, r) is dim 32mt + 8(r/4) + 4hi + r%4
+  if (row_ok) {
+    float* dqo = a.dq + (((int64_t)b * S + i) * a.Hq + h) * D;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(dqo + 32 * mt + 8 * j + 4 * hi) =
+            f32x4{dq[mt][4 * j] * a.scale, dq[mt][4 * j + 1] * a.scale, dq[mt][4 * j + 2] * a.scale,
+                  dq[mt][4 * j + 3] * a.scale};
+  }
+}
+
+// ====================================================================== launch
+template <int D, int G>
+hipError_t launch_kv(const BwdArgs& a, hipStream_t stream) {
+  const int64_t nkb = (a.S + CfgKV<D, G>::KB - 1) / CfgKV<D, G>::KB;
+  hipLaunchKernelGGL((bwd_dkdv<D, G>), dim3((unsigned)((int64_t)a.B * a.Hkv * nkb)), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_q(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq<D, G>), dim3((unsigned)((int64_t)a.B * a.Hkv * a.nq)), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_block_k(int group) { return 32 * (8 / group); }
+
+hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int B, int S, int Hq, int D,
+                            hipStream_t stream) {
+  const int64_t threads = (int64_t)B * S * Hq * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (D == 128)
+    hipLaunchKernelGGL((bwd_delta<128>), grid, dim3(256), 0, stream, static_cast<const __bf16*>(out),
+                       static_cast<const __bf16*>(dout), delta, B, S, Hq);
+  else
+    hipLaunchKernelGGL((bwd_delta<64>), grid, dim3(256), 0, stream, static_cast<const __bf16*>(out),
+                       static_cast<const __bf16*>(dout), delta, B, S, Hq);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  if (a.D == 128) return G == 1 ? launch_kv<128, 1>(a, stream) : G == 2 ? launch_kv<128, 2>(a, stream) : launch_kv<128, 4>(a, stream);
+  return G == 1 ? launch_kv<64, 1>(a, stream) : G == 2 ? launch_kv<64, 2>(a, stream) : launch_kv<64, 4>(a, stream);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  if (a.D == 128) return G == 1 ? launch_q<128, 1>(a, stream) : G == 2 ? launch_q<128, 2>(a, stream) : launch_q<128, 4>(a, stream);
+  return G == 1 ? launch_q<64, 1>(a, stream) : G == 2 ? launch_q<64, 2>(a, stream) : launch_q<64, 4>(a, stream);
+}
+
+}  // namespace ha

@@ -199,7 +199,7 @@ struct Dma {
   }
 };
 
-template <int D, int G, bool PRE>
+template <int D, int G, bool PRE, bool LSE>
 __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   using C = CfgB<D, G>;
   using TL = Tile<D>;
@@ -380,8 +380,8 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // way, so the result is the softmax up to rounding. negm holds -m in the units of the S
   // accumulator (log2 units when q is prescaled, raw otherwise) and is the C operand of
   // each tile's first MFMA.
+  float mref = 0.f;  // the row's reference m (0 unless the careful pass moved it)
   if (redo) {
-    float m = 0.f;
     f32x16 negm = f32x16{};
     l = 0.f;
 #pragma unroll
@@ -407,7 +407,7 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
         if (!PRE) mx *= c;
         float sh = fmaxf(mx, __builtin_amdgcn_logf(l));
         sh = (bad && sh > -INFINITY) ? sh : 0.f;
-        m += sh;
+        mref += sh;
         // alpha <= 1/l for l > 0 (sh >= log2 l), and l >= kLo outside the first tile, so
         // it cannot overflow; with l = 0 nothing has been accumulated (O = 0) and it is 0
         const float alpha = l == 0.f ? 0.f : __builtin_amdgcn_exp2f(-sh);
@@ -428,6 +428,12 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     }
   }
 
+  // row log-sum-exp of the natural-unit scores for a training backward: with the scores in
+  // log2 units, log2 sum_j 2^s_j = m + log2(l)
+  if constexpr (LSE) {
+    if (row_ok && hi == 0)
+      a.lse[((int64_t)b * a.Hq + h) * S + i] = (mref + __builtin_amdgcn_logf(l)) * 0.693147180559945309f;
+  }
   if (row_ok) {
     const float inv = 1.f / l;
     __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * S + i) * a.Hq + h) * D;
@@ -562,10 +568,16 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((attn_f32<D, G, false>), grid, block, 0, stream, a);
   } else {
     const dim3 block(CfgB<D, G>::NT);
-    if (a.q_prescaled)
-      hipLaunchKernelGGL((attn_bf16<D, G, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_bf16<D, G, false>), grid, block, 0, stream, a);
+    if (a.lse) {
+      if (a.q_prescaled)
+        hipLaunchKernelGGL((attn_bf16<D, G, true, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_bf16<D, G, false, true>), grid, block, 0, stream, a);
+    } else if (a.q_prescaled) {
+      hipLaunchKernelGGL((attn_bf16<D, G, true, false>), grid, block, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_bf16<D, G, false, false>), grid, block, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -242,7 +242,7 @@ ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const v
 }
 
 ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const void* v, const int32_t* row_limit,
-                   const int32_t* ranges, void* out, bool prescaled, hipStream_t stream) {
+                   const int32_t* ranges, void* out, bool prescaled, hipStream_t stream, float* lse = nullptr) {
   ha::AttnArgs a{};
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
@@ -261,6 +261,7 @@ ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const vo
   a.scale_log2e = q_prescale(d);
   a.q_prescaled = prescaled;
   a.f32 = d->dtype == HA_DTYPE_F32;
+  a.lse = lse;
   return check_launch(ha::launch_attn(a, stream), stream, "attention");
 }
 
@@ -286,6 +287,53 @@ Workspace workspace_layout(const ha_attn_desc* d, bool prologue) {
   }
   w.total = at;
   return w;
+}
+
+// ---------------------------------------------------------------- training
+ha_status check_train(const ha_attn_desc* d) {
+  if (d->dtype != HA_DTYPE_BF16) return fail(HA_ERR_UNSUPPORTED, "training entry points take bf16 tensors");
+  const int group = d->n_q_heads / d->n_kv_heads;
+  if (group > 4) return fail(HA_ERR_UNSUPPORTED, "training: n_q_heads / n_kv_heads = %d; supported: 1, 2, 4", group);
+  return HA_OK;
+}
+
+bool has_norm(const ha_prologue_desc* p) { return p && p->q_norm_weight; }
+
+struct BwdWorkspace {
+  size_t row_limit, ranges, q_rot, k_rot, delta, dq_rot, dk_rot, dwq, dwk, dw_scratch, total;
+};
+
+BwdWorkspace bwd_workspace_layout(const ha_attn_desc* d, bool norm) {
+  int bq, bk, nq, nk;
+  tile_shape(d, &bq, &bk, &nq, &nk);
+  const size_t B = d->batch, S = d->seq_len, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+  BwdWorkspace w{};
+  size_t at = 0;
+  auto take = [&](size_t& field, size_t bytes) {
+    field = at;
+    at = round256(at + bytes);
+  };
+  take(w.row_limit, B * S * 4);
+  take(w.ranges, B * nq * 2 * 4);
+  take(w.q_rot, B * S * Hq * D * 2);
+  take(w.k_rot, B * S * Hkv * D * 2);
+  take(w.delta, B * Hq * S * 4);
+  take(w.dq_rot, B * S * Hq * D * 4);
+  take(w.dk_rot, B * S * Hkv * D * 4);
+  if (norm) {
+    take(w.dwq, B * S * D * 4);
+    take(w.dwk, B * S * D * 4);
+    take(w.dw_scratch, (size_t)ha::dw_scratch_floats((int)D) * 4);
+  }
+  w.total = at;
+  return w;
+}
+
+ha_status check_workspace(const void* workspace, size_t have, size_t need) {
+  if (!workspace) return fail(HA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(HA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (have < need) return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  return HA_OK;
 }
 
 }  // namespace
@@ -379,8 +427,12 @@ ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const voi
   return st == HA_OK ? ok() : st;
 }
 
-ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
-                      const void* v, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
+                   const void* v, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   ha_status st = check_desc(desc);
   if (st != HA_OK) return st;
   if (pro && (st = check_prologue(desc, pro)) != HA_OK) return st;
@@ -389,10 +441,7 @@ ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
       (st = check_tensor(v, "v")) != HA_OK || (st = check_tensor(out, "out")) != HA_OK)
     return st;
   const Workspace w = workspace_layout(desc, pro != nullptr);
-  if (!workspace) return fail(HA_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(HA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (workspace_bytes < w.total)
-    return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+  if ((st = check_workspace(workspace, workspace_bytes, w.total)) != HA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   int32_t* row_limit = reinterpret_cast<int32_t*>(ws + w.row_limit);
   int32_t* ranges = reinterpret_cast<int32_t*>(ws + w.ranges);
@@ -407,8 +456,142 @@ ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
     qa = qr;
     ka = kr;
   }
-  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, pro != nullptr, s);
+  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, pro != nullptr, s, lse);
   return st == HA_OK ? ok() : st;
+}
+
+}  // namespace
+
+extern "C" {
+
+ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
+                      const void* v, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd(desc, pro, q, k, v, out, nullptr, workspace, workspace_bytes, stream);
+}
+
+ha_status ha_attn_fwd_lse(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
+                          const void* v, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if ((st = check_train(desc)) != HA_OK) return st;
+  if (!empty(desc) && (!lse || !aligned(lse, 4))) return fail(HA_ERR_INVALID_ARG, "lse must be a 4-byte aligned pointer");
+  return attn_fwd(desc, pro, q, k, v, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t ha_attn_bwd_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro) {
+  if (check_desc(desc) != HA_OK) return 0;
+  return bwd_workspace_layout(desc, has_norm(pro)).total;
+}
+
+ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
+                      const void* v, const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                      void* dv, float* dw_q, float* dw_k, void* workspace, size_t workspace_bytes, void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if ((st = check_train(desc)) != HA_OK) return st;
+  if (pro && (st = check_prologue(desc, pro)) != HA_OK) return st;
+  if (desc->q_prescaled != 0) return fail(HA_ERR_INVALID_ARG, "ha_attn_bwd: desc->q_prescaled must be 0");
+  const bool norm = has_norm(pro);
+  if (norm != (dw_q != nullptr) || norm != (dw_k != nullptr))
+    return fail(HA_ERR_INVALID_ARG, "dw_q and dw_k are required exactly when the prologue has RMSNorm");
+  if (norm && (!aligned(dw_q, 4) || !aligned(dw_k, 4))) return fail(HA_ERR_ALIGNMENT, "dw_q, dw_k must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = desc->head_dim;
+  if (empty(desc)) {
+    // no tokens: the weight gradients are empty sums
+    if (norm) {
+      if ((st = check_launch(ha::launch_dw_reduce(nullptr, 0, D, nullptr, dw_q, s), s, "dw")) != HA_OK) return st;
+      if ((st = check_launch(ha::launch_dw_reduce(nullptr, 0, D, nullptr, dw_k, s), s, "dw")) != HA_OK) return st;
+    }
+    return ok();
+  }
+  const void* tensors[] = {q, k, v, out, dout, dq, dk, dv};
+  const char* names[] = {"q", "k", "v", "out", "dout", "dq", "dk", "dv"};
+  for (int t = 0; t < 8; ++t)
+    if ((st = check_tensor(tensors[t], names[t])) != HA_OK) return st;
+  if (!lse || !aligned(lse, 4)) return fail(HA_ERR_INVALID_ARG, "lse must be a 4-byte aligned pointer");
+  const BwdWorkspace w = bwd_workspace_layout(desc, norm);
+  if ((st = check_workspace(workspace, workspace_bytes, w.total)) != HA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* row_limit = reinterpret_cast<int32_t*>(ws + w.row_limit);
+  int32_t* ranges = reinterpret_cast<int32_t*>(ws + w.ranges);
+  void* q_rot = ws + w.q_rot;
+  void* k_rot = ws + w.k_rot;
+  float* delta = reinterpret_cast<float*>(ws + w.delta);
+  float* dq_rot = reinterpret_cast<float*>(ws + w.dq_rot);
+  float* dk_rot = reinterpret_cast<float*>(ws + w.dk_rot);
+
+  if ((st = run_classify(desc, nullptr, ranges, row_limit, s)) != HA_OK) return st;
+  // q' = scale log2(e) (normalised, rotated q) and the rotated k, as the forward used them
+  ha_prologue_desc plain{};
+  plain.rope_kind = HA_ROPE_NONE;
+  if ((st = run_prologue(desc, pro ? pro : &plain, q, k, q_rot, k_rot, q_prescale(desc), s)) != HA_OK) return st;
+  const int B = desc->batch, S = desc->seq_len, Hq = desc->n_q_heads, Hkv = desc->n_kv_heads;
+  if ((st = check_launch(ha::launch_bwd_delta(out, dout, delta, B, S, Hq, D, s), s, "backward delta")) != HA_OK)
+    return st;
+  ha::BwdArgs a{};
+  int bq, bk, nq, nk;
+  tile_shape(desc, &bq, &bk, &nq, &nk);
+  a.q = q_rot;
+  a.k = k_rot;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.row_limit = row_limit;
+  a.ranges = ranges;
+  a.dq = dq_rot;
+  a.dk = dk_rot;
+  a.dv = dv;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.nq = nq;
+  a.scale = (float)softmax_scale(desc);
+  if ((st = check_launch(ha::launch_bwd_dkdv(a, s), s, "backward dK dV")) != HA_OK) return st;
+  if ((st = check_launch(ha::launch_bwd_dq(a, s), s, "backward dQ")) != HA_OK) return st;
+  // through the rotary embedding and RMSNorm to the inputs
+  ha::PrologueBwdArgs p{};
+  p.dq_rot = dq_rot;
+  p.dk_rot = dk_rot;
+  p.q_in = q;
+  p.k_in = k;
+  p.dq = dq;
+  p.dk = dk;
+  p.rotate = pro && pro->rope_kind != HA_ROPE_NONE;
+  if (p.rotate) {
+    p.positions = pro->positions;
+    p.cos_sin = pro->cos_sin;
+    p.n_axes = n_axes_of(pro->rope_kind);
+    p.n_pos = pro->n_pos;
+    axis_table(pro, D, p.axis);
+  }
+  if (norm) {
+    p.wq = pro->q_norm_weight;
+    p.wk = pro->k_norm_weight;
+    p.eps = pro->eps;
+    p.dwq_part = reinterpret_cast<float*>(ws + w.dwq);
+    p.dwk_part = reinterpret_cast<float*>(ws + w.dwk);
+  }
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  if ((st = check_launch(ha::launch_prologue_bwd(p, s), s, "backward prologue")) != HA_OK) return st;
+  if (norm) {
+    float* scratch = reinterpret_cast<float*>(ws + w.dw_scratch);
+    if ((st = check_launch(ha::launch_dw_reduce(p.dwq_part, (int64_t)B * S, D, scratch, dw_q, s), s, "dw_q")) !=
+        HA_OK)
+      return st;
+    if ((st = check_launch(ha::launch_dw_reduce(p.dwk_part, (int64_t)B * S, D, scratch, dw_k, s), s, "dw_k")) !=
+        HA_OK)
+      return st;
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -61,7 +61,60 @@ struct AttnArgs {
   float scale_log2e;         // softmax scale * log2(e)
   int32_t q_prescaled;       // 1: q already carries scale_log2e
   int32_t f32;
+  float* lse;                // [B][Hq][S] row log-sum-exp (natural log), or null
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+// ---- backward (ha_attn_bwd.hip, ha_prologue.hip)
+
+// Key block of the dK/dV kernel: 32 keys per wave, 8 / G waves per query head.
+int bwd_block_k(int group);
+
+struct BwdArgs {
+  const void* q;             // q' = scale * log2(e) * (rotated q), bf16 [B][S][Hq][D]
+  const void* k;             // rotated k, bf16 [B][S][Hkv][D]
+  const void* v;             // bf16 [B][S][Hkv][D]
+  const void* dout;          // bf16 [B][S][Hq][D]
+  const float* lse;          // [B][Hq][S], natural log
+  const float* delta;        // [B][Hq][S]: dout . out per row
+  const int32_t* row_limit;  // [B][S]
+  const int32_t* ranges;     // [B][nq][2], query blocks of attn_block_q rows
+  float* dq;                 // gradient of the rotated q, fp32 [B][S][Hq][D]
+  float* dk;                 // gradient of the rotated k, fp32 [B][S][Hkv][D]
+  void* dv;                  // bf16 [B][S][Hkv][D]
+  int32_t B, S, Hq, Hkv, D, nq;
+  float scale;               // softmax scale
+};
+hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int B, int S, int Hq, int D,
+                            hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+
+// Rotary and RMSNorm backward: d(rotated) fp32 -> d(input) in the tensors' dtype, plus per
+// token sums over heads of dy * x * r for the norm weights' gradient.
+struct PrologueBwdArgs {
+  const float* dq_rot;  // [B][S][Hq][D]
+  const float* dk_rot;  // [B][S][Hkv][D]
+  const void* q_in;     // the forward prologue's inputs (needed with RMSNorm)
+  const void* k_in;
+  void* dq;             // [B][S][Hq][D]
+  void* dk;             // [B][S][Hkv][D]
+  float* dwq_part;      // [B*S][D] or null (no RMSNorm)
+  float* dwk_part;
+  const int32_t* positions;
+  const float* cos_sin;
+  const float* wq;
+  const float* wk;
+  int32_t B, S, Hq, Hkv, D, n_axes, n_pos;
+  int32_t rotate;
+  float eps;
+  int32_t f32;
+  uint8_t axis[64];
+};
+hipError_t launch_prologue_bwd(const PrologueBwdArgs& a, hipStream_t stream);
+// dw[d] = sum over rows of part[row][d] (fp32), for rows in [0, n), in a fixed order;
+// scratch holds dw_scratch_floats(D) floats of per-workgroup sums (unused when n == 0)
+int dw_scratch_floats(int D);
+hipError_t launch_dw_reduce(const float* part, int64_t n, int D, float* scratch, float* dw, hipStream_t stream);
 
 }  // namespace ha

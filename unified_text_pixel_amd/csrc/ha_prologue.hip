@@ -118,3 +118,145 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
 }
 
 }  // namespace ha
+
+// ---------------------------------------------------------------- backward
+//
+// Gradient of the prologue's inputs from the gradient of its outputs (fp32, before any
+// q prescale). Per head row, with g the output gradient:
+//   rotary:  the pair rotation is orthogonal, so its input gradient is g rotated by minus
+//            the angle: (g1 c + g2 s, g2 c - g1 s)
+//   RMSNorm: y = x r w, r = (mean(x^2) + eps)^(-1/2); with u = dy * w,
+//            dx = r u - x r^3 mean(x u),  and the weight gradient collects dy * x r
+// One workgroup per token, D/16 threads per head row as in the forward; the token's weight
+// gradient (its heads' terms staged in LDS and summed in head order) goes to one row of a
+// per-token partial array, which launch_dw_reduce then sums over tokens.
+namespace ha {
+namespace {
+
+template <int D, bool F32>
+__global__ __launch_bounds__(1024) void prologue_bwd_kernel(PrologueBwdArgs a) {
+  constexpr int HALF = D / 2;
+  constexpr int TPR = D / 16;
+  constexpr int MAXROWS = 1024 / TPR;  // head rows one workgroup can hold
+  __shared__ float2 cs[HALF];
+  __shared__ float contrib[MAXROWS][D];  // this token's dy * x * r per head row
+  const int64_t token = blockIdx.x;
+
+  if (a.rotate) {
+    for (int t = threadIdx.x; t < HALF; t += blockDim.x) {
+      int p = a.positions[token * a.n_axes + a.axis[t]];
+      p = min(max(p, 0), a.n_pos - 1);
+      cs[t] = reinterpret_cast<const float2*>(a.cos_sin)[(int64_t)p * HALF + t];
+    }
+  }
+  __syncthreads();
+
+  const int row = threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row < a.Hq + a.Hkv) {
+    const bool isq = row < a.Hq;
+    const int h = isq ? row : row - a.Hq;
+    const int64_t base = (token * (isq ? a.Hq : a.Hkv) + h) * D;
+    const float* gin = (isq ? a.dq_rot : a.dk_rot) + base;
+    const float* w = isq ? a.wq : a.wk;
+
+    float g1[8], g2[8];
+    load8<true>(gin, 8 * c, g1);
+    load8<true>(gin, HALF + 8 * c, g2);
+    if (a.rotate) {
+      for (int e = 0; e < 8; ++e) {
+        const float2 t = cs[8 * c + e];
+        const float y1 = g1[e] * t.x + g2[e] * t.y;
+        const float y2 = g2[e] * t.x - g1[e] * t.y;
+        g1[e] = y1;
+        g2[e] = y2;
+      }
+    }
+    if (w) {
+      float x1[8], x2[8];
+      load8<F32>(isq ? a.q_in : a.k_in, base + 8 * c, x1);
+      load8<F32>(isq ? a.q_in : a.k_in, base + HALF + 8 * c, x2);
+      float ss = 0.f, xu = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        ss += x1[e] * x1[e] + x2[e] * x2[e];
+        xu += x1[e] * g1[e] * w[8 * c + e] + x2[e] * g2[e] * w[HALF + 8 * c + e];
+      }
+      for (int o = 1; o < TPR; o <<= 1) {
+        ss += __shfl_xor(ss, o);
+        xu += __shfl_xor(xu, o);
+      }
+      const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+      const float k3 = r * r * r * xu / (float)D;
+      for (int e = 0; e < 8; ++e) {
+        contrib[row][8 * c + e] = g1[e] * x1[e] * r;
+        contrib[row][HALF + 8 * c + e] = g2[e] * x2[e] * r;
+        g1[e] = r * g1[e] * w[8 * c + e] - x1[e] * k3;
+        g2[e] = r * g2[e] * w[HALF + 8 * c + e] - x2[e] * k3;
+      }
+    }
+    void* out = isq ? a.dq : a.dk;
+    store8<F32>(out, base + 8 * c, g1);
+    store8<F32>(out, base + HALF + 8 * c, g2);
+  }
+  if (a.dwq_part) {
+    // the token's weight gradients: sums over its q heads and over its k heads, in order
+    __syncthreads();
+    for (int t = threadIdx.x; t < 2 * D; t += blockDim.x) {
+      const int d = t % D;
+      const bool q = t < D;
+      float s = 0.f;
+      for (int r = q ? 0 : a.Hq, e = q ? a.Hq : a.Hq + a.Hkv; r < e; ++r) s += contrib[r][d];
+      (q ? a.dwq_part : a.dwk_part)[token * D + d] = s;
+    }
+  }
+}
+
+// dw[d] = sum over n rows of part[row][d], in two passes of fixed order: kDwBlocks
+// workgroups each sum a contiguous chunk of rows into out[block][d], then one workgroup
+// sums those. 1024 threads: 1024 / D threads per column, strided over the chunk.
+constexpr int kDwBlocks = 256;
+
+__global__ __launch_bounds__(1024) void dw_sum_kernel(const float* part, int64_t n, int D, float* out) {
+  __shared__ float acc[1024];
+  const int d = threadIdx.x % D, per = blockDim.x / D, j = threadIdx.x / D;
+  const int64_t chunk = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t r0 = (int64_t)blockIdx.x * chunk, r1 = min(n, r0 + chunk);
+  float s = 0.f;
+  for (int64_t r = r0 + j; r < r1; r += per) s += part[r * D + d];
+  acc[threadIdx.x] = s;
+  __syncthreads();
+  if (j == 0) {
+    for (int k = 1; k < per; ++k) s += acc[k * D + d];
+    out[(int64_t)blockIdx.x * D + d] = s;
+  }
+}
+
+template <int D, bool F32>
+hipError_t launch_bwd(const PrologueBwdArgs& a, hipStream_t stream) {
+  const int threads = ((a.Hq + a.Hkv) * (D / 16) + 63) / 64 * 64;
+  hipLaunchKernelGGL((prologue_bwd_kernel<D, F32>), dim3((unsigned)((int64_t)a.B * a.S)), dim3(threads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prologue_bwd(const PrologueBwdArgs& a, hipStream_t stream) {
+  if (a.D == 128) return a.f32 ? launch_bwd<128, true>(a, stream) : launch_bwd<128, false>(a, stream);
+  return a.f32 ? launch_bwd<64, true>(a, stream) : launch_bwd<64, false>(a, stream);
+}
+
+int dw_scratch_floats(int D) { return kDwBlocks * D; }
+
+hipError_t launch_dw_reduce(const float* part, int64_t n, int D, float* scratch, float* dw, hipStream_t stream) {
+  if (n == 0) {  // empty sum: one pass over no rows writes the zeros
+    hipLaunchKernelGGL(dw_sum_kernel, dim3(1), dim3(1024), 0, stream, part, n, D, dw);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(dw_sum_kernel, dim3(kDwBlocks), dim3(1024), 0, stream, part, n, D, scratch);
+  hipLaunchKernelGGL(dw_sum_kernel, dim3(1), dim3(1024), 0, stream, (const float*)scratch, (int64_t)kDwBlocks, D,
+                     dw);
+  return hipGetLastError();
+}
+
+}  // namespace ha
