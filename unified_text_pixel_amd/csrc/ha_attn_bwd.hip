@@ -56,25 +56,40 @@ __device__ inline float bpermute(int src_lane, float x) {
 
 // Copies rows [row0, row0 + rows) of a row-major global tensor (row stride gstride bytes,
 // rows clamped to [0, rmax]) into LDS, ROWB bytes per row made of segments of D elements
-// (one per head), each swizzled by the row within the tile. 1 KB per DMA instruction;
-// instruction ins is issued by wave ins mod 8 (wave is wave-uniform).
+// (one per head), each swizzled by the row within the tile. 1 KB per DMA instruction:
+// lane L writes bytes 16L of it, i.e. row RPI*ins + L*16/ROWB of the tile, segment
+// (L*16 % ROWB) / 2D, physical chunk L % CPR, which holds logical chunk (L % CPR) ^ (row
+// mod CPR). Instruction ins is issued by wave ins mod 8; the lane's part of the address is
+// computed once.
 template <int D, int ROWB, int NINS>
-__device__ __attribute__((always_inline)) inline void dma_rows(const char* gbase, int64_t gstride, int row0, int rmax, char* lds, int wave,
-                                int lane) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int j = 0; j < (NINS + 7) / 8; ++j) {
-    const int ins = wave + 8 * j;  // a run-time index keeps the LDS address out of constant folding
-    if (NINS % 8 != 0 && ins >= NINS) continue;
-    const int off = ins * 1024 + 16 * lane;
-    const int rho = off / ROWB, rem = off % ROWB;
-    const int seg = rem / (2 * D), pc = (rem % (2 * D)) / 16;
-    const int lc = pc ^ (rho & (CPR - 1));
-    const int r = min(max(row0 + rho, 0), rmax);
-    const char* src = gbase + r * gstride + seg * (2 * D) + lc * 16;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + ins * 1024), 16, 0, 0);
+struct RowDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 1024 / ROWB;  // rows per instruction
+  int rho, segb, pc;                        // the lane's row in an instruction, segment bytes, chunk
+
+  __device__ inline void init(int lane) {
+    rho = (16 * lane) / ROWB;
+    segb = ((16 * lane) % ROWB) / (2 * D) * (2 * D);
+    pc = ((16 * lane) % (2 * D)) / 16;
   }
-}
+
+  __device__ __attribute__((always_inline)) inline void issue(const char* gbase, int64_t gstride, int row0,
+                                                                int rmax, char* lds, int wave) const {
+#pragma unroll
+    for (int j = 0; j < (NINS + 7) / 8; ++j) {
+      const int ins = wave + 8 * j;  // run-time: keeps the LDS address out of constant folding
+      if (NINS % 8 != 0 && ins >= NINS) continue;
+      const int row = ins * RPI + rho;
+      const int r = min(max(row0 + row, 0), rmax);
+      const char* src = gbase + r * gstride + segb + ((pc ^ (row & (CPR - 1))) * 16);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + ins * 1024), 16, 0, 0);
+    }
+  }
+};
+
+// s_waitcnt vmcnt(0) through the builtin, so the compiler's own wait tracking knows that
+// every vector memory operation has completed (gfx9 encoding: expcnt 7, lgkmcnt 15)
+__device__ __attribute__((always_inline)) inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // (batch * KV heads) pair and block slot of workgroup x: XCD-aware when the pairs split
 // evenly over the 8 XCDs (workgroups go round-robin to XCDs), so each XCD's L2 holds the
@@ -154,8 +169,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   const int64_t kvstride = (int64_t)a.Hkv * D * 2;
   const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * S * a.Hkv + g) * D * 2;
   const char* vbase = static_cast<const char*>(a.v) + ((int64_t)b * S * a.Hkv + g) * D * 2;
-  dma_rows<D, 2 * D, C::KVBYTES / 1024>(kbase, kvstride, k0, S - 1, kt, wave, lane);
-  dma_rows<D, 2 * D, C::KVBYTES / 1024>(vbase, kvstride, k0, S - 1, vt, wave, lane);
+  {
+    RowDma<D, 2 * D, C::KVBYTES / 1024> kvd;
+    kvd.init(lane);
+    kvd.issue(kbase, kvstride, k0, S - 1, kt, wave);
+    kvd.issue(vbase, kvstride, k0, S - 1, vt, wave);
+  }
 
   // step s = 32 rows starting at qrow0 + 32 s; active when its query block attends a key
   // >= k0 (then it attends k0: rows see prefixes) and some row is >= 0
@@ -178,65 +197,101 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   const int32_t* lim_b = a.row_limit + (int64_t)b * S;
   // step s into a tile pair; the lane's row (ln) values into registers: log2(e) lse,
   // delta and the row's key limit (0 for rows before the sequence, which see no key)
+  RowDma<D, C::QROWB, C::QBYTES / 1024> qd_dma;
+  qd_dma.init(lane);
+  // raw loads only: using a loaded value before the step's DMA has landed would make the
+  // compiler wait for that DMA (vector memory operations complete in order)
   auto fetch = [&](int s, char* qd, char* od, float& lr, float& dr, int& mr) __attribute__((always_inline)) {
     const int r0 = qrow0 + 32 * s;
-    dma_rows<D, C::QROWB, C::QBYTES / 1024>(qbase, qstride, r0, S - 1, qd, wave, lane);
-    dma_rows<D, C::QROWB, C::QBYTES / 1024>(obase, qstride, r0, S - 1, od, wave, lane);
-    const int i = r0 + ln;
-    const int ic = max(i, 0);
-    lr = lse_h[ic] * kLog2e;
+    const int ic = max(r0 + ln, 0);
+    lr = lse_h[ic];
     dr = del_h[ic];
-    mr = i >= 0 ? lim_b[ic] : 0;
+    mr = lim_b[ic];
+    qd_dma.issue(qbase, qstride, r0, S - 1, qd, wave);
+    qd_dma.issue(obase, qstride, r0, S - 1, od, wave);
+  };
+  // a step needs the per-pair mask unless every row of it is inside the sequence and
+  // attends every key of the block (keys [0, 64 kfull) of its query block, and < S)
+  auto masked_step = [&](int s) __attribute__((always_inline)) {
+    const int qb = s / C::SUB;
+    const int kfull = a.ranges[((int64_t)b * nq + qb) * 2 + 0];
+    return !(qrow0 + 32 * s >= 0 && k0 + C::KB <= kfull * BK && k0 + C::KB <= S);
   };
 
   // A/B operand reads of rows (q' or dO row ln, or K/V row 32 ksl + ln): chunk 2kk + hi of
-  // the row sits at (2kk) ^ kx
-  const int kx = hi ^ (ln & (C::CPR - 1));
-  // transposing reads: lane t of 16-lane group G16 points at row 16KS + 8rr + 4(G16 >> 1)
-  // + t/4 and dims 32mt + 16(G16 & 1) + 4(t & 3)
-  const int g16 = lane >> 4, t16 = lane & 15;
-  const int vrow = 4 * (g16 >> 1) + (t16 >> 2);
-  const int vclow = 2 * (g16 & 1) + ((t16 & 3) >> 1);
-  const int vhalf = 8 * (t16 & 1);
+  // the row sits at (2kk) ^ kx, kx = hi ^ (ln mod CPR). Transposing reads: lane t of
+  // 16-lane group G16 points at row 16KS + 8rr + 4(G16 >> 1) + t/4 and dims 32mt + 16(G16 & 1)
+  // + 4(t & 3).
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16{};
 
-  auto compute = [&](const char* qc, const char* oc, float lr, float dr, int mr) __attribute__((always_inline)) {
-    // S = Q' K^T and dP = dO V^T: rows x keys, lane = key, register r = row 8(r/4) + 4hi + r%4
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-    const char* qrow = qc + (ln * G + hg) * (2 * D);
-    const char* orow = oc + (ln * G + hg) * (2 * D);
-    const char* krow = kt + (32 * ksl + ln) * (2 * D);
-    const char* vrowp = vt + (32 * ksl + ln) * (2 * D);
+  // The lane's row constants enter the first MFMA of S and of dP as an extra A column
+  // (rows x 16, only k = 0, 1 used: -log2(e) lse and -delta split into bf16 hi + lo, exact
+  // to 2^-16 relative) against a B column of ones, so S' = Q' K^T - log2(e) lse and
+  // dP' = dO V^T - delta arrive per (row, key) without moving per-row values across lanes.
+  bf16x8 ones = {};
+  if (hi == 0) ones[0] = ones[1] = static_cast<__bf16>(1.0f);
+  auto split_col = [&](float x) __attribute__((always_inline)) {
+    bf16x8 c = {};
+    const __bf16 h = static_cast<__bf16>(-x);
+    if (hi == 0) {
+      c[0] = h;
+      c[1] = static_cast<__bf16>(-x - static_cast<float>(h));
+    }
+    return c;
+  };
+
+  auto compute = [&](const char* qc, const char* oc, float lr, float dr, int mr, int s, bool masked)
+                     __attribute__((always_inline)) {
+    // the lane's LDS addresses are rebuilt each step from an opaque copy of the lane id:
+    // kept live across the loop they would not fit in registers
+    int lo = lane;
+    __asm__ volatile("" : "+v"(lo));
+    const int lnx = lo & 31, hix = lo >> 5;
+    const int kxx = hix ^ (lnx & (C::CPR - 1));
+    // S' and dP': rows x keys, lane = key, register r = row 8(r/4) + 4hi + r%4
+    f32x16 sacc = mfma(split_col(lr * kLog2e), ones, f32x16{});
+    f32x16 pacc = mfma(split_col(dr), ones, f32x16{});
+    if (qrow0 + 32 * s + ln < 0) mr = 0;  // rows before the sequence see no key
+    const char* qrow = qc + (lnx * G + hg) * (2 * D);
+    const char* orow = oc + (lnx * G + hg) * (2 * D);
+    const char* krow = kt + (32 * ksl + lnx) * (2 * D);
+    const char* vrowp = vt + (32 * ksl + lnx) * (2 * D);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int off = ((2 * kk) ^ kx) * 16;
+      const int off = ((2 * kk) ^ kxx) * 16;
       sacc = mfma(*reinterpret_cast<const bf16x8*>(qrow + off), *reinterpret_cast<const bf16x8*>(krow + off), sacc);
       pacc = mfma(*reinterpret_cast<const bf16x8*>(orow + off), *reinterpret_cast<const bf16x8*>(vrowp + off), pacc);
     }
-    // P = exp2(S - log2(e) lse) on allowed (row, key) pairs, dZ = P (dP - delta); both to
-    // bf16 with rows 16KS .. 16KS + 15 in register order (the A-operand k order)
+    // P = exp2(S') on allowed (row, key) pairs, dZ = P dP'; both to bf16 with rows
+    // 16KS .. 16KS + 15 in register order (the A-operand k order). Only steps that need
+    // the mask fetch each row's key limit from the lane that loaded it.
     bf16x8 pa[2], za[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int src = 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float l2 = bpermute(src, lr);
-      const float de = bpermute(src, dr);
-      const int lim = __builtin_bit_cast(int, bpermute(src, __builtin_bit_cast(float, mr)));
-      const float p = key < lim ? __builtin_amdgcn_exp2f(sacc[r] - l2) : 0.f;
+      float p = __builtin_amdgcn_exp2f(sacc[r]);
+      if (masked) {
+        const int src = 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int lim = __builtin_bit_cast(int, bpermute(src, __builtin_bit_cast(float, mr)));
+        p = key < lim ? p : 0.f;
+      }
       pa[r >> 3][r & 7] = static_cast<__bf16>(p);
-      za[r >> 3][r & 7] = static_cast<__bf16>(p * (pacc[r] - de));
+      za[r >> 3][r & 7] = static_cast<__bf16>(p * pacc[r]);
     }
     // dV += P^T dO, dK += dZ^T Q' (B: dO / q' rows of this head gathered per dims 32mt..)
+    const int g16x = lo >> 4, t16x = lo & 15;
+    const int vrx = 4 * (g16x >> 1) + (t16x >> 2);
+    const int vclx = 2 * (g16x & 1) + ((t16x & 3) >> 1);
+    const int vhx = 8 * (t16x & 1);
 #pragma unroll
     for (int KS = 0; KS < 2; ++KS) {
-      const int rl = 16 * KS + vrow, ru = rl + 8;
+      const int rl = 16 * KS + vrx, ru = rl + 8;
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) {
-        const int cl = (((4 * mt + vclow) ^ (rl & (C::CPR - 1))) * 16) + vhalf;
-        const int cu = (((4 * mt + vclow) ^ (ru & (C::CPR - 1))) * 16) + vhalf;
+        const int cl = (((4 * mt + vclx) ^ (rl & (C::CPR - 1))) * 16) + vhx;
+        const int cu = (((4 * mt + vclx) ^ (ru & (C::CPR - 1))) * 16) + vhx;
         const char* ol = oc + (rl * G + hg) * (2 * D) + cl;
         const char* ou = oc + (ru * G + hg) * (2 * D) + cu;
         const bf16x4 dol = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ol);
@@ -258,20 +313,23 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   int s = next_step(-1);
   if (s >= 0) fetch(s, q0, o0, la, da, ma);
   while (s >= 0) {
+    // the step's mask flag is read before the wait, so using it waits for nothing issued later
     const int s1 = next_step(s);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bool m0 = masked_step(s);
+    wait_vm();
     __syncthreads();
     if (s1 >= 0) fetch(s1, q1, o1, lb, db, mb);
-    compute(q0, o0, la, da, ma);
+    compute(q0, o0, la, da, ma, s, m0);
     if (s1 < 0) break;
     const int s2 = next_step(s1);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bool m1 = masked_step(s1);
+    wait_vm();
     __syncthreads();
     if (s2 >= 0) fetch(s2, q0, o0, la, da, ma);
-    compute(q1, o1, lb, db, mb);
+    compute(q1, o1, lb, db, mb, s1, m1);
     s = s2;
   }
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K/V DMA of an item with no step
+  wait_vm();  // K/V DMA of an item with no step
 
   // dK for the rotated k: scale * sum dZ q = ln(2) * sum dZ q' (q' = scale log2(e) q)
 #pragma unroll
@@ -366,8 +424,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
   const int64_t kvstride = (int64_t)a.Hkv * D * 2;
   const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * S * a.Hkv + g) * D * 2;
   const char* vbase = static_cast<const char*>(a.v) + ((int64_t)b * S * a.Hkv + g) * D * 2;
-  dma_rows<D, 2 * D, C::TBYTES / 1024>(kbase, kvstride, 0, S - 1, k0, wave, lane);
-  dma_rows<D, 2 * D, C::TBYTES / 1024>(vbase, kvstride, 0, S - 1, v0, wave, lane);
+  RowDma<D, 2 * D, C::TBYTES / 1024> kvd;
+  kvd.init(lane);
+  kvd.issue(kbase, kvstride, 0, S - 1, k0, wave);
+  kvd.issue(vbase, kvstride, 0, S - 1, v0, wave);
 
   // the row's q' and dO as B operands (dims 16kk + 8hi .. +8), its log2(e) lse and delta
   bf16x8 qf[D / 16], of[D / 16];
@@ -410,11 +470,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
     const char* const vc = PAR ? v1 : v0;
     char* const kn = PAR ? k0 : k1;
     char* const vn = PAR ? v0 : v1;
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm();
     __syncthreads();
     if (t + 1 < kend) {
-      dma_rows<D, 2 * D, C::TBYTES / 1024>(kbase, kvstride, (t + 1) * BK, S - 1, kn, wave, lane);
-      dma_rows<D, 2 * D, C::TBYTES / 1024>(vbase, kvstride, (t + 1) * BK, S - 1, vn, wave, lane);
+      kvd.issue(kbase, kvstride, (t + 1) * BK, S - 1, kn, wave);
+      kvd.issue(vbase, kvstride, (t + 1) * BK, S - 1, vn, wave);
     }
     f32x16 st[2], pt[2];
     rows_times(kc, qf, st);  // S^T = K Q'^T
