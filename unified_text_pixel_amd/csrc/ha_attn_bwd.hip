@@ -441,28 +441,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
   const float l2 = a.lse[((int64_t)b * a.Hq + h) * S + ic] * kLog2e;
   const float de = a.delta[((int64_t)b * a.Hq + h) * S + ic];
 
-  const int krow = ln;
-  const int kx = hi ^ (krow & (C::CPR - 1));
-  const int g16 = lane >> 4, t16 = lane & 15;
-  const int vrow = 4 * (g16 >> 1) + (t16 >> 2);
-  const int vclow = 2 * (g16 & 1) + ((t16 & 3) >> 1);
-  const int vhalf = 8 * (t16 & 1);
-
   f32x16 dq[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
-
-  // X^T (keys x rows) = T B^T for the 64 rows of tile buffer tb and the row fragments bf
-  auto rows_times = [&](const char* tb, const bf16x8 (&bf)[D / 16], f32x16 (&s)[2]) __attribute__((always_inline)) {
-    s[0] = s[1] = f32x16{};
-    const char* r0 = tb + krow * (2 * D);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int off = ((2 * kk) ^ kx) * 16;
-      s[0] = mfma(*reinterpret_cast<const bf16x8*>(r0 + off), bf[kk], s[0]);
-      s[1] = mfma(*reinterpret_cast<const bf16x8*>(r0 + 32 * 2 * D + off), bf[kk], s[1]);
-    }
-  };
 
   auto step = [&](auto par_tag, int t) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
@@ -476,21 +457,41 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
       kvd.issue(kbase, kvstride, (t + 1) * BK, S - 1, kn, wave);
       kvd.issue(vbase, kvstride, (t + 1) * BK, S - 1, vn, wave);
     }
-    f32x16 st[2], pt[2];
-    rows_times(kc, qf, st);  // S^T = K Q'^T
-    rows_times(vc, of, pt);  // dP^T = V dO^T
+    // LDS addresses from an opaque copy of the lane id, rebuilt each step (kept live
+    // across the loop they would not fit in registers)
+    int lo = lane;
+    __asm__ volatile("" : "+v"(lo));
+    const int lnx = lo & 31, hix = lo >> 5;
+    const int kxx = hix ^ (lnx & (C::CPR - 1));
+    // per 32-key half: S^T = K Q'^T and dP^T = V dO^T (keys x rows, lane = row), then
     // dZ^T = P^T (dP^T - delta) on allowed keys, to bf16 in B-operand order (keys
     // 16KS .. 16KS + 15 of the tile in register order)
     bf16x8 zf[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 st = f32x16{}, pt = f32x16{};
+      const char* kr = kc + (32 * kt + lnx) * (2 * D);
+      const char* vr = vc + (32 * kt + lnx) * (2 * D);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int off = ((2 * kk) ^ kxx) * 16;
+        st = mfma(*reinterpret_cast<const bf16x8*>(kr + off), qf[kk], st);
+        pt = mfma(*reinterpret_cast<const bf16x8*>(vr + off), of[kk], pt);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = t * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float p = key < lim ? __builtin_amdgcn_exp2f(st[kt][r] - l2) : 0.f;
-        zf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pt[kt][r] - de));
+        const int key = t * BK + 32 * kt + 8 * (r >> 2) + 4 * hix + (r & 3);
+        const float p = key < lim ? __builtin_amdgcn_exp2f(st[r] - l2) : 0.f;
+        zf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pt[r] - de));
       }
-    // dQ^T += K^T dZ^T: A = K^T (dims 32mt .., keys of step KS) gathered from LDS
+    }
+    // dQ^T += K^T dZ^T: A = K^T (dims 32mt .., keys of step KS) gathered from LDS; lane t
+    // of 16-lane group G16 points at key 16KS + 8rr + 4(G16 >> 1) + t/4, dims 32mt +
+    // 16(G16 & 1) + 4(t & 3)
+    const int g16 = lo >> 4, t16 = lo & 15;
+    const int vrow = 4 * (g16 >> 1) + (t16 >> 2);
+    const int vclow = 2 * (g16 & 1) + ((t16 & 3) >> 1);
+    const int vhalf = 8 * (t16 & 1);
 #pragma unroll
     for (int KS = 0; KS < BK / 16; ++KS) {
       const int rl = 16 * KS + vrow, ru = rl + 8;
@@ -498,9 +499,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
       for (int mt = 0; mt < D / 32; ++mt) {
         const char* pl = kc + rl * (2 * D) + (((4 * mt + vclow) ^ (rl & (C::CPR - 1))) * 16) + vhalf;
         const char* pu = kc + ru * (2 * D) + (((4 * mt + vclow) ^ (ru & (C::CPR - 1))) * 16) + vhalf;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pl);
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pu);
-        dq[mt] = mfma(__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7), zf[KS], dq[mt]);
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pl);
+        const bf16x4 up4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pu);
+        dq[mt] = mfma(__builtin_shufflevector(lo4, up4, 0, 1, 2, 3, 4, 5, 6, 7), zf[KS], dq[mt]);
       }
     }
   };
