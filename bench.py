@@ -14,7 +14,11 @@ timed step, which gives the attention kernel's own duration for the MFMA rooflin
 the prologue's for its HBM roofline. Three copies of the inputs are cycled so the 256 MB
 Infinity Cache cannot serve a step from the previous one.
 
-    python bench.py [--steps K] [--warmup W] [--workload hd2048] [--no-cpu-baseline]
+The training backward (ha_attn_bwd after ha_attn_fwd_lse) is timed on its own afterwards
+and reported under "backward" (8 d FLOP per allowed pair and query head); it is not part
+of the step.
+
+    python bench.py [--steps K] [--warmup W] [--workload hd2048] [--no-cpu-baseline] [--no-backward]
 """
 from __future__ import annotations
 
@@ -102,6 +106,56 @@ def cpu_baseline(w, x, target_s=12.0):
                       f"attention), {elapsed:.1f} s; host os.cpu_count()={os.cpu_count()}"}
 
 
+def backward_leg(w, x, dev, useful_fwd, stream, warmup, steps, nsets):
+    """Training backward (ha_attn_bwd: rebuilt prologue, dK/dV, dQ, rotary and RMSNorm
+    backward) after a forward with lse, timed alone with HIP events on the launch stream.
+    Algorithmic work: 8 d FLOP per allowed (query, key) pair and query head (dV, dP, dQ and
+    dK products; the recomputed scores are not counted), twice the forward's."""
+    import torch
+    from unified_text_pixel_amd import api, binding as B
+    desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments)
+    cs = api.rope_table(w.rope_theta, w.head_dim, w.seq_len) if w.rope != "none" else None
+    pro = B.PrologueDesc(w.rope, dev["positions"], cs, 0 if cs is None else cs.shape[0],
+                         dev["w_q"], dev["w_k"], w.norm_eps, w.mrope_sections)
+    ws = torch.empty(max(B.ha_attn_workspace_bytes(desc, pro), B.ha_attn_bwd_workspace_bytes(desc, pro)),
+                     dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    sets = []
+    for _ in range(nsets):
+        o = {"q": dev["q"].clone(), "k": dev["k"].clone(), "v": dev["v"].clone(),
+             "out": torch.empty_like(dev["q"]),
+             "lse": torch.empty((w.batch, w.n_q_heads, w.seq_len), dtype=torch.float32, device="cuda"),
+             "dout": torch.randn(dev["q"].shape, generator=gen, device="cuda").to(torch.bfloat16),
+             "dq": torch.empty_like(dev["q"]), "dk": torch.empty_like(dev["k"]), "dv": torch.empty_like(dev["v"])}
+        norm = w.qk_norm
+        o["dwq"] = torch.empty(w.head_dim, device="cuda") if norm else None
+        o["dwk"] = torch.empty(w.head_dim, device="cuda") if norm else None
+        B.ha_attn_fwd_lse(desc, pro, o["q"], o["k"], o["v"], o["out"], o["lse"], ws, stream=stream)
+        sets.append(o)
+
+    def bwd(o):
+        B.ha_attn_bwd(desc, pro, o["q"], o["k"], o["v"], o["out"], o["lse"], o["dout"], o["dq"], o["dk"],
+                      o["dv"], o["dwq"], o["dwk"], ws, stream=stream)
+
+    for i in range(max(1, warmup // 2)):
+        bwd(sets[i % nsets])
+    n = max(5, steps // 4)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(stream)
+        bwd(sets[i % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    flop = 2.0 * useful_fwd
+    tf = flop / (float(np.median(ms)) / 1e3) / 1e12
+    return {"ms": {"median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+                   "p90": float(np.percentile(ms, 90))},
+            "gflop": flop / 1e9, "flop_per_pair_head": 8 * w.head_dim,
+            "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "calls": n}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +164,7 @@ def main():
     ap.add_argument("--workload", default="hd2048")
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -223,6 +278,8 @@ def main():
                               "unit": "GB/s", "frac": pro_gbps / HBM_PEAK_GBPS},
         "attn_kernel_sha": kernel_sha(),
     }
+    if not args.no_backward and w.dtype == "bf16":
+        rec["backward"] = backward_leg(w, x, dev, useful, stream, args.warmup, args.steps, args.sets)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, x)
