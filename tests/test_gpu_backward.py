@@ -170,3 +170,27 @@ def test_backward_hd2048_one_group():
     check("hd2048 dq", got["dq"][1, :, heads], want["dq"][0, :, heads])
     check("hd2048 dk", got["dk"][1, :, 3], want["dk"][0, :, 3])
     check("hd2048 dv", got["dv"][1, :, 3], want["dv"][0, :, 3])
+
+
+def test_autograd_matches_direct_calls():
+    """api.hybrid_attention_train under torch autograd gives exactly what the direct calls
+    give (same kernels), including the norm-weight gradients."""
+    from unified_text_pixel_amd import api
+    w = SMALL["edit_small"]
+    x = W.generate(w)
+    dev = to_device(x)
+    attn = api.HybridAttention(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, "bf16",
+                               x.segments, rope=w.rope, positions=dev["positions"], theta=w.rope_theta,
+                               mrope_sections=w.mrope_sections, q_norm_weight=dev["w_q"],
+                               k_norm_weight=dev["w_k"], eps=w.norm_eps)
+    q, k, v = (dev[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    wq, wk = dev["w_q"].clone().requires_grad_(True), dev["w_k"].clone().requires_grad_(True)
+    dout = torch.from_numpy(output_grad(w)).to(torch.bfloat16).cuda()
+    out = api.hybrid_attention_train(attn, q, k, v, wq, wk)
+    out.backward(dout)
+    out2, lse = attn.forward_train(dev["q"], dev["k"], dev["v"])
+    ref = attn.backward(dev["q"], dev["k"], dev["v"], out2, lse, dout)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), out2)
+    for got, want in zip((q.grad, k.grad, v.grad, wq.grad, wk.grad), ref):
+        assert torch.equal(got, want)

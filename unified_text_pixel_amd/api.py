@@ -57,6 +57,51 @@ class HybridAttention:
         B.ha_attn_fwd(self.desc, self.pro, q, k, v, out, self.workspace, stream=stream)
         return out
 
+    # ---- training (bf16, Hq / Hkv in {1, 2, 4})
+    def forward_train(self, q, k, v, stream=None):
+        """(out, lse): the forward plus each row's log-sum-exp [B][Hq][S] for backward()."""
+        out = torch.empty(self.shape, dtype=q.dtype, device=q.device)
+        b, s, hq, _ = self.shape
+        lse = torch.empty((b, hq, s), dtype=torch.float32, device=q.device)
+        B.ha_attn_fwd_lse(self.desc, self.pro, q, k, v, out, lse, self.workspace, stream=stream)
+        return out, lse
+
+    def backward(self, q, k, v, out, lse, dout, stream=None):
+        """(dq, dk, dv, dw_q, dw_k) for the output gradient dout; dw_* are None without
+        q/k RMSNorm. The backward workspace is allocated on first use and kept."""
+        if getattr(self, "bwd_workspace", None) is None:
+            n = B.ha_attn_bwd_workspace_bytes(self.desc, self.pro)
+            self.bwd_workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        norm = self.pro is not None and self.pro.c.q_norm_weight is not None
+        dwq = torch.empty(self.shape[3], dtype=torch.float32, device=q.device) if norm else None
+        dwk = torch.empty(self.shape[3], dtype=torch.float32, device=q.device) if norm else None
+        B.ha_attn_bwd(self.desc, self.pro, q, k, v, out, lse, dout.contiguous(), dq, dk, dv, dwq, dwk,
+                      self.bwd_workspace, stream=stream)
+        return dq, dk, dv, dwq, dwk
+
+
+class _HybridAttentionFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, attn, q, k, v, w_q, w_k):
+        out, lse = attn.forward_train(q, k, v)
+        ctx.attn = attn
+        ctx.save_for_backward(q, k, v, out, lse)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv, dwq, dwk = ctx.attn.backward(q, k, v, out, lse, dout.to(out.dtype))
+        return None, dq, dk, dv, dwq, dwk
+
+
+def hybrid_attention_train(attn: HybridAttention, q, k, v, w_q=None, w_k=None):
+    """out = attn(q, k, v) recorded for torch autograd: out.backward() (or a loss built on it)
+    fills q.grad, k.grad, v.grad and, when attn normalises q and k, the grads of the norm
+    weight tensors w_q, w_k (the ones attn was built with)."""
+    return _HybridAttentionFn.apply(attn, q, k, v, w_q, w_k)
+
 
 def hybrid_attention(q, k, v, segments, **kw) -> torch.Tensor:
     b, s, hq, d = q.shape
