@@ -14,11 +14,15 @@ timed step, which gives the attention kernel's own duration for the MFMA rooflin
 the prologue's for its HBM roofline. Three copies of the inputs are cycled so the 256 MB
 Infinity Cache cannot serve a step from the previous one.
 
+"prefix_step" times a denoising step that reuses the causal text prefix (its rotated q, k
+and output rows) from an earlier step: the prologue and attention rows from the text end.
+
 The training backward (ha_attn_bwd after ha_attn_fwd_lse) is timed on its own afterwards
 and reported under "backward" (8 d FLOP per allowed pair and query head); it is not part
 of the step.
 
     python bench.py [--steps K] [--warmup W] [--workload hd2048] [--no-cpu-baseline] [--no-backward]
+                    [--no-prefix]
 """
 from __future__ import annotations
 
@@ -106,6 +110,44 @@ def cpu_baseline(w, x, target_s=12.0):
                       f"attention), {elapsed:.1f} s; host os.cpu_count()={os.cpu_count()}"}
 
 
+def prefix_leg(w, x, sets, desc, pro, stream, step, warmup, steps):
+    """A denoising step that reuses the causal text prefix: the prologue from the text end
+    (ha_qk_prologue_from) and the attention rows from the text end (ha_attn_fwd_planned_from)
+    over buffers a whole step filled; the tile plan is the same every step. Timed like the
+    whole step, HIP events around each call."""
+    import torch
+    from unified_text_pixel_amd import binding as B
+    seg = x.segments[0]
+    p = int(seg[0][1]) if int(seg[0][2]) == 0 and int(seg[0][0]) == 0 else 0
+    for s in sets:
+        step(s)
+
+    def run(s, ev=None):
+        if ev:
+            ev[0].record(stream)
+        B.ha_qk_prologue_from(desc, pro, s["q"], s["k"], s["qr"], s["kr"], p, stream)
+        if ev:
+            ev[1].record(stream)
+        B.ha_attn_fwd_planned_from(desc, s["qr"], s["kr"], s["v"], s["lim"], s["ranges"], s["out"], p,
+                                   stream)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        run(sets[i % len(sets)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        run(sets[i % len(sets)], evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return {"begin": p, "ms_per_step": t0.elapsed_time(t1) / steps,
+            "prologue_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+            "attn_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
+
+
 def backward_leg(w, x, dev, useful_fwd, stream, warmup, steps, nsets):
     """Training backward (ha_attn_bwd: rebuilt prologue, dK/dV, dQ, rotary and RMSNorm
     backward) after a forward with lse, timed alone with HIP events on the launch stream.
@@ -165,6 +207,7 @@ def main():
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-prefix", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -278,6 +321,8 @@ def main():
                               "unit": "GB/s", "frac": pro_gbps / HBM_PEAK_GBPS},
         "attn_kernel_sha": kernel_sha(),
     }
+    if not args.no_prefix:
+        rec["prefix_step"] = prefix_leg(w, x, sets, desc, pro, stream, step, args.warmup, args.steps)
     if not args.no_backward and w.dtype == "bf16":
         rec["backward"] = backward_leg(w, x, dev, useful, stream, args.warmup, args.steps, args.sets)
     if not args.no_cpu_baseline:

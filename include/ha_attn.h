@@ -174,6 +174,29 @@ ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
                       const void* k, const void* v, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- step-invariant prefix
+ * Causal rows see only keys at or before themselves (HiDream-O1 atlas page, "How it works":
+ * text and condition tokens are causal). So a causal prefix of the sequence (the text
+ * tokens and markers at its front) never sees the generation tokens after it, and its
+ * outputs and its k, v stay the same across the denoising steps of one image (model card,
+ * "What this model is": the same layout for every step). This reuse follows from the mask;
+ * the pages do not describe it. A caller that keeps the previous step's rotated q, k and the
+ * output of such a prefix [0, p) recomputes only what follows it: */
+
+/* ha_qk_prologue on tokens [token_begin, seq_len) of every batch item; the rest of q_out,
+ * k_out is not touched. 0 <= token_begin <= seq_len. */
+ha_status ha_qk_prologue_from(const ha_attn_desc* desc, const ha_prologue_desc* pro,
+                              const void* q_in, const void* k_in, void* q_out, void* k_out,
+                              int32_t token_begin, void* stream);
+
+/* ha_attn_fwd_planned for the query rows [row_begin, seq_len) only: the query blocks that
+ * hold them are computed (from all of q, k, v: the prefix's q, k, v must be in place), and
+ * out rows below row_begin are not written. Exact when rows below row_begin do not attend
+ * to changed keys, which holds for a causal prefix. 0 <= row_begin <= seq_len. */
+ha_status ha_attn_fwd_planned_from(const ha_attn_desc* desc, const void* q, const void* k,
+                                   const void* v, const int32_t* row_limit, const int32_t* ranges,
+                                   void* out, int32_t row_begin, void* stream);
+
 /* ---------------------------------------------------------------- training
  * The pages train these models end to end (HiDream-O1 atlas page, "How it works";
  * HunyuanImage 3.0 digest, training stages); the backward below is the derivative of the

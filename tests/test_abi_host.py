@@ -25,7 +25,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = U.load_library()
     names = declared_functions()
-    assert len(names) == 13 and sorted(B.EXPORTS) == names
+    assert len(names) == 15 and sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
     assert U.ha_abi_version() == 2
@@ -72,6 +72,8 @@ def test_bad_descriptor_rejected_everywhere(kw, status, text):
         lambda: U.ha_attn_fwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0),
         lambda: U.ha_qk_prologue(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, stream=0),
         lambda: U.ha_attn_fwd_lse(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0),
+        lambda: U.ha_attn_fwd_planned_from(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0),
+        lambda: U.ha_qk_prologue_from(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, 0, stream=0),
         lambda: U.ha_attn_bwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                               FAKE, 1 << 30, stream=0),
     ]
@@ -240,3 +242,18 @@ def test_backward_workspace_layout():
     # bf16 rebuilt q, k + fp32 gradients of both + per-row delta
     assert plain >= tokens * 40 * 128 * (2 + 4) + tokens * 32 * 4
     assert normed - plain >= 2 * tokens * 128 * 4
+
+
+def test_prefix_entry_points_check_ranges():
+    d = desc()
+    for bad in (-1, 81):
+        with pytest.raises(U.HAError) as e:
+            U.ha_attn_fwd_planned_from(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bad, stream=0)
+        assert e.value.status == B.HA_ERR_INVALID_ARG and "row_begin" in str(e.value)
+        with pytest.raises(U.HAError) as e:
+            U.ha_qk_prologue_from(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, bad, stream=0)
+        assert e.value.status == B.HA_ERR_INVALID_ARG and "token_begin" in str(e.value)
+    # nothing left to compute: no launch, no error
+    U.ha_attn_fwd_planned_from(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 80, stream=0)
+    U.ha_qk_prologue_from(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, 80, stream=0)
+    assert U.ha_last_error() == ""

@@ -50,6 +50,9 @@ class HybridAttention:
                                       k_norm_weight, eps, mrope_sections)
         nbytes = B.ha_attn_workspace_bytes(self.desc, self.pro)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        self._args = (batch, seq_len, n_q_heads, n_kv_heads, head_dim, dtype, segments, scale)
+        self._pro_args = (rope, positions, cos_sin, q_norm_weight, k_norm_weight, eps, mrope_sections)
+        self._steps = None
 
     def __call__(self, q, k, v, out=None, stream=None):
         if out is None:
@@ -79,6 +82,76 @@ class HybridAttention:
         B.ha_attn_bwd(self.desc, self.pro, q, k, v, out, lse, dout.contiguous(), dq, dk, dv, dwq, dwk,
                       self.bwd_workspace, stream=stream)
         return dq, dk, dv, dwq, dwk
+
+
+    # ---- denoising steps over a step-invariant causal prefix
+    def forward_from(self, q, k, v, begin, stream=None):
+        """The forward of (q, k, v), recomputing only what tokens >= begin can change: the
+        prologue from token begin on and the attention rows from begin on, over buffers kept
+        in this object (rotated q and k, tile plan, output). The first call, or begin == 0,
+        runs the whole path. Later calls are exact when the q, k, v rows below begin are the
+        ones the previous call saw and no row below begin attends to a later token
+        (prefix_is_invariant; a causal text prefix qualifies), which is checked. Returns the kept output
+        tensor (overwritten by the next call)."""
+        if not 0 <= begin <= self.shape[1]:
+            raise ValueError(f"begin {begin} outside [0, {self.shape[1]}]")
+        if not prefix_is_invariant(self.desc._seg_np, self.shape[1], begin):
+            raise ValueError(f"rows below begin {begin} attend to later tokens: their outputs "
+                             "would change with them")
+        if self._steps is None:
+            self._steps = self._plan(q)
+            begin = 0
+        st = self._steps
+        if begin == 0:
+            B.ha_classify_tiles(st["desc"], None, st["ranges"], st["lim"], stream)
+        if st["pro"] is not None:
+            B.ha_qk_prologue_from(st["desc"], st["pro"], q, k, st["qr"], st["kr"], begin, stream)
+            qr, kr = st["qr"], st["kr"]
+        else:
+            qr, kr = q, k
+        B.ha_attn_fwd_planned_from(st["desc"], qr, kr, v, st["lim"], st["ranges"], st["out"], begin,
+                                   stream)
+        return st["out"]
+
+    def _plan(self, q):
+        batch, seq_len, hq, hkv, d, dtype, segments, scale = self._args
+        rope, positions, cos_sin, wq, wk, eps, sections = self._pro_args
+        st = {"pro": None}
+        if self.pro is not None:
+            # the prologue writes q scaled by softmax scale * log2(e), taken as is by attention
+            st["desc"] = B.AttnDesc(batch, seq_len, hq, hkv, d, dtype, segments, scale, q_prescaled=1)
+            cs = self.pro._keep[1]
+            st["pro"] = B.PrologueDesc(rope, positions, cs, 0 if cs is None else cs.shape[0], wq, wk,
+                                       eps, sections, q_out_scale=B.ha_q_prescale(st["desc"]))
+            st["qr"] = torch.empty(self.shape, dtype=q.dtype, device=q.device)
+            st["kr"] = torch.empty((batch, seq_len, hkv, d), dtype=q.dtype, device=q.device)
+        else:
+            st["desc"] = self.desc
+        _, _, nq, _ = B.ha_tile_shape(st["desc"])
+        st["ranges"] = torch.empty((batch, nq, 2), dtype=torch.int32, device=q.device)
+        st["lim"] = torch.empty((batch, seq_len), dtype=torch.int32, device=q.device)
+        st["out"] = torch.empty(self.shape, dtype=q.dtype, device=q.device)
+        return st
+
+
+def prefix_is_invariant(segments, seq_len: int, p: int) -> bool:
+    """True when no query row below p attends to a key at or after p, in any batch item of
+    a segment table [B][n_seg][3] (start, length, kind: 0 causal, 1 full, 2 image): rows
+    below p then give the same output whatever tokens >= p hold. A causal row i sees keys
+    <= i, so causal segments never break it; a full segment's rows see every key, so one
+    that starts below p < seq_len does; an image segment's rows see keys below its end, so
+    one that p splits does."""
+    if not 0 <= p <= seq_len:
+        return False
+    seg = np.asarray(segments, dtype=np.int64).reshape(-1, 3)
+    for st, ln, kind in seg:
+        if ln <= 0:
+            continue
+        if kind == 1 and st < p < seq_len:
+            return False
+        if kind == 2 and st < p < st + ln:
+            return False
+    return True
 
 
 class _HybridAttentionFn(torch.autograd.Function):

@@ -98,7 +98,8 @@ __device__ inline float exp_tile(const f32x16 (&s)[2], float c, bf16x8 (&pf)[4])
 // Work item of this workgroup: XCD-aware order when the (batch, KV head) pairs split
 // evenly over the 8 XCDs (workgroups go round-robin to XCDs), so each XCD's L2 keeps the
 // K/V of its own pairs; query blocks run from the last to the first (the cheap causal
-// text blocks at the front of the sequence finish the grid).
+// text blocks at the front of the sequence finish the grid). Only the last nq_run blocks
+// of each pair are work items (all of them unless a caller reuses a step-invariant prefix).
 struct Item {
   int b, g, qb;
 };
@@ -108,11 +109,11 @@ __device__ inline Item work_item(const AttnArgs& a) {
   int bg, slot;
   if (nbg % 8 == 0) {
     const int xcd = item % 8, s = item / 8;
-    bg = xcd + 8 * (s / a.nq);
-    slot = s % a.nq;
+    bg = xcd + 8 * (s / a.nq_run);
+    slot = s % a.nq_run;
   } else {
-    bg = item / a.nq;
-    slot = item % a.nq;
+    bg = item / a.nq_run;
+    slot = item % a.nq_run;
   }
   return {bg / a.Hkv, bg % a.Hkv, a.nq - 1 - slot};
 }
@@ -431,10 +432,10 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // row log-sum-exp of the natural-unit scores for a training backward: with the scores in
   // log2 units, log2 sum_j 2^s_j = m + log2(l)
   if constexpr (LSE) {
-    if (row_ok && hi == 0)
+    if (i >= a.row_begin && hi == 0)
       a.lse[((int64_t)b * a.Hq + h) * S + i] = (mref + __builtin_amdgcn_logf(l)) * 0.693147180559945309f;
   }
-  if (row_ok) {
+  if (i >= a.row_begin) {  // also excludes rows before the sequence (row_begin >= 0)
     const float inv = 1.f / l;
     __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * S + i) * a.Hq + h) * D;
 #pragma unroll
@@ -544,7 +545,7 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
   }
 
   const float inv = 1.f / wave_pair_sum(l);  // per-lane partial sums over the two key halves
-  if (row_ok) {
+  if (i >= a.row_begin) {  // also excludes rows before the sequence (row_begin >= 0)
     float* orow = static_cast<float*>(a.out) + (((int64_t)b * S + i) * a.Hq + h) * D;
     for (int mt = 0; mt < D / 32; ++mt)
       for (int j = 0; j < 4; ++j) {
@@ -558,7 +559,7 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
 // ====================================================================== launch
 template <int D, int G>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-  const int64_t items = (int64_t)a.B * a.Hkv * a.nq;
+  const int64_t items = (int64_t)a.B * a.Hkv * a.nq_run;
   const dim3 grid((unsigned)items);
   if (a.f32) {
     const dim3 block(CfgF<D, G>::NT);

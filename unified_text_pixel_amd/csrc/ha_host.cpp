@@ -216,7 +216,7 @@ double softmax_scale(const ha_attn_desc* d) {
 float q_prescale(const ha_attn_desc* d) { return (float)(softmax_scale(d) * 1.4426950408889634074); }
 
 ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const void* q_in, const void* k_in,
-                       void* q_out, void* k_out, float q_scale, hipStream_t stream) {
+                       void* q_out, void* k_out, float q_scale, hipStream_t stream, int token_begin = 0) {
   ha::PrologueArgs a{};
   a.q_in = q_in;
   a.k_in = k_in;
@@ -237,12 +237,14 @@ ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const v
   a.eps = p->eps;
   a.q_scale = q_scale;
   a.f32 = d->dtype == HA_DTYPE_F32;
+  a.token_begin = token_begin;
   axis_table(p, d->head_dim, a.axis);
   return check_launch(ha::launch_prologue(a, stream), stream, "prologue");
 }
 
 ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const void* v, const int32_t* row_limit,
-                   const int32_t* ranges, void* out, bool prescaled, hipStream_t stream, float* lse = nullptr) {
+                   const int32_t* ranges, void* out, bool prescaled, hipStream_t stream, float* lse = nullptr,
+                   int row_begin = 0) {
   ha::AttnArgs a{};
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
@@ -262,6 +264,10 @@ ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const vo
   a.q_prescaled = prescaled;
   a.f32 = d->dtype == HA_DTYPE_F32;
   a.lse = lse;
+  // the query blocks holding rows >= row_begin: blocks end at S, so that is the last
+  // ceil((S - row_begin) / bq) of them
+  a.nq_run = (int)cdiv(d->seq_len - row_begin, bq);
+  a.row_begin = row_begin;
   return check_launch(ha::launch_attn(a, stream), stream, "attention");
 }
 
@@ -463,6 +469,41 @@ ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const 
 }  // namespace
 
 extern "C" {
+
+ha_status ha_qk_prologue_from(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q_in,
+                              const void* k_in, void* q_out, void* k_out, int32_t token_begin, void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if ((st = check_prologue(desc, pro)) != HA_OK) return st;
+  if (token_begin < 0 || token_begin > desc->seq_len)
+    return fail(HA_ERR_INVALID_ARG, "token_begin %d outside [0, seq_len %d]", token_begin, desc->seq_len);
+  if (empty(desc) || token_begin == desc->seq_len) return ok();
+  if ((st = check_tensor(q_in, "q_in")) != HA_OK || (st = check_tensor(k_in, "k_in")) != HA_OK ||
+      (st = check_tensor(q_out, "q_out")) != HA_OK || (st = check_tensor(k_out, "k_out")) != HA_OK)
+    return st;
+  st = run_prologue(desc, pro, q_in, k_in, q_out, k_out, pro->q_out_scale > 0.f ? pro->q_out_scale : 1.f,
+                    static_cast<hipStream_t>(stream), token_begin);
+  return st == HA_OK ? ok() : st;
+}
+
+ha_status ha_attn_fwd_planned_from(const ha_attn_desc* desc, const void* q, const void* k, const void* v,
+                                   const int32_t* row_limit, const int32_t* ranges, void* out, int32_t row_begin,
+                                   void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if (row_begin < 0 || row_begin > desc->seq_len)
+    return fail(HA_ERR_INVALID_ARG, "row_begin %d outside [0, seq_len %d]", row_begin, desc->seq_len);
+  if (empty(desc) || row_begin == desc->seq_len) return ok();
+  if ((st = check_tensor(q, "q")) != HA_OK || (st = check_tensor(k, "k")) != HA_OK ||
+      (st = check_tensor(v, "v")) != HA_OK || (st = check_tensor(out, "out")) != HA_OK)
+    return st;
+  if (!row_limit || !ranges) return fail(HA_ERR_INVALID_ARG, "row_limit and ranges are required");
+  if (!aligned(row_limit, 4) || !aligned(ranges, 4))
+    return fail(HA_ERR_ALIGNMENT, "row_limit and ranges must be 4-byte aligned");
+  st = run_attn(desc, q, k, v, row_limit, ranges, out, desc->q_prescaled == 1, static_cast<hipStream_t>(stream),
+                nullptr, row_begin);
+  return st == HA_OK ? ok() : st;
+}
 
 ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
                       const void* v, void* out, void* workspace, size_t workspace_bytes, void* stream) {

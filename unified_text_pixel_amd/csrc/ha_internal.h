@@ -42,6 +42,7 @@ struct PrologueArgs {
   float eps;
   float q_scale;   // q outputs are multiplied by this before rounding
   int32_t f32;     // 1: fp32 tensors, 0: bf16
+  int32_t token_begin;  // tokens [token_begin, S) of every batch item are processed
   uint8_t axis[64];  // rotary axis of pair i
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
@@ -62,6 +63,8 @@ struct AttnArgs {
   int32_t q_prescaled;       // 1: q already carries scale_log2e
   int32_t f32;
   float* lse;                // [B][Hq][S] row log-sum-exp (natural log), or null
+  int32_t nq_run;            // compute the last nq_run query blocks of each (batch, KV head)
+  int32_t row_begin;         // rows below it are computed with their block but not written
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 

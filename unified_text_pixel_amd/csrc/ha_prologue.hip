@@ -48,7 +48,9 @@ __global__ __launch_bounds__(1024) void prologue_kernel(PrologueArgs a) {
   constexpr int HALF = D / 2;
   constexpr int TPR = D / 16;  // threads per head row
   __shared__ float2 cs[HALF];
-  const int64_t token = blockIdx.x;  // b * S + s
+  // token b * S + s, s in [token_begin, S)
+  const int run = a.S - a.token_begin;
+  const int64_t token = (int64_t)(blockIdx.x / run) * a.S + a.token_begin + blockIdx.x % run;
 
   if (a.rotate) {
     for (int t = threadIdx.x; t < HALF; t += blockDim.x) {
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(1024) void prologue_kernel(PrologueArgs a) {
 template <int D, bool F32>
 hipError_t launch(const PrologueArgs& a, hipStream_t stream) {
   const int threads = ((a.Hq + a.Hkv) * (D / 16) + 63) / 64 * 64;
-  hipLaunchKernelGGL((prologue_kernel<D, F32>), dim3((unsigned)((int64_t)a.B * a.S)),
+  hipLaunchKernelGGL((prologue_kernel<D, F32>), dim3((unsigned)((int64_t)a.B * (a.S - a.token_begin))),
                      dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
