@@ -33,5 +33,5 @@ from .pipeline import prologue, hot_path, hot_path_rows
 from .backward import (attention_lse, attention_backward, rope_backward, rms_norm_backward,
                        path_lse, path_backward)
 
-SEG_CAUSAL, SEG_FULL, SEG_GCA = 0, 1, 2
+SEG_CAUSAL, SEG_FULL, SEG_GCA, SEG_GEN = 0, 1, 2, 3
 LABEL_SKIP, LABEL_FULL, LABEL_PARTIAL = 0, 1, 2

@@ -7,9 +7,10 @@ so that the two can check each other. Same readings as the rest of the oracle:
   rotary   pair (i, i + d/2) rotated by pos[axis(i)] * base^(-2i/d); axis(i) deals the
            pairs to the axes in turn within each axis's section count
            (HunyuanImage 3.0 digest, generalized 2D RoPE; model card, mRoPE [24,20,20])
-  mask     causal j <= i; full always; image segment j <= i or same segment
+  mask     causal j <= i; full always; image segment j <= i or same segment; never a
+           key of a Gen Image (multi-image training) that ended at or before i
            (HiDream-O1 atlas page, "How it works"; HunyuanImage 3.0 digest,
-           "Generalized Causal Attention")
+           "Generalized Causal Attention" and its multi-generation training paragraph)
   softmax  over allowed keys of scale * q.k, scale = 1/sqrt(d)
 """
 from __future__ import annotations
@@ -39,12 +40,14 @@ def _kind_and_segment(table, t):
 
 
 def _allowed(table, i, j):
+    kind_j, seg_j = _kind_and_segment(table, j)
+    if kind_j == 3 and i >= int(table[seg_j][0]) + int(table[seg_j][1]):
+        return False  # key in a Gen Image that token i comes after
     kind_i, seg_i = _kind_and_segment(table, i)
     if kind_i == 0:
         return j <= i
     if kind_i == 1:
         return True
-    _kind_j, seg_j = _kind_and_segment(table, j)
     return j <= i or seg_j == seg_i
 
 

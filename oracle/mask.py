@@ -16,6 +16,14 @@ Rules, one per segment kind, taken row by row as the pages state them:
               M[i, j] = (j <= i) or (segment(j) == segment(i)).
               HunyuanImage 3.0 digest, "Generalized Causal Attention", the core rule;
               HunyuanImage 3.0 summary page, "Key claims".
+  GEN (3)     a Gen Image of a multi-image HunyuanImage 3.0 training sequence (one that is
+              being denoised while later tokens follow it): its own rows follow the GCA
+              rule, and no token after it attends to it, so the mask gets a hole below the
+              diagonal: M[i, j] = False for j in a GEN segment that ends at or before i,
+              whatever the kind of row i. HunyuanImage 3.0 digest, "Generalized Causal
+              Attention", the multi-generation training complication and Figure 4(b).
+              Reading: "subsequent tokens" are the tokens after the segment's end, so the
+              image's own rows keep seeing it; later Gen Images are subsequent tokens too.
 Adjacent GCA segments are distinct images and are not merged.
 """
 from __future__ import annotations
@@ -48,10 +56,14 @@ def mask_rows(segments: np.ndarray, seq_len: int, rows) -> np.ndarray:
             M[r] = j <= i
         elif kind == 1:
             M[r] = True
-        elif kind == 2:
+        elif kind in (2, 3):
             M[r] = (j <= i) | (seg == idx)
         else:
             raise ValueError(f"unknown segment kind {kind}")
+        # the hole: Gen Images that ended at or before token i
+        for start, length, kind_g in table:
+            if kind_g == 3 and start + length <= i:
+                M[r, start:start + length] = False
     return M
 
 

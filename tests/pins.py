@@ -21,7 +21,7 @@ import workloads as W
 from oracle.brute import brute_force
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-C, F, G = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA
+C, F, G, GEN = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA, W.SEG_GEN
 
 
 def small_workload(segs, hq=4, hkv=2, d=16, rope="mrope", sections=(4, 2, 2), norm=True,
@@ -34,8 +34,10 @@ def small_workload(segs, hq=4, hkv=2, d=16, rope="mrope", sections=(4, 2, 2), no
 
 def closed_form_pairs(segments, S):
     """Allowed pairs from arithmetic series, one term per segment: a causal segment
-    [a, a+L) contributes sum_{i=a}^{a+L-1} (i+1); a full one L*S; an image (GCA)
-    segment L*(a+L), since each of its rows sees every key before the segment end."""
+    [a, a+L) contributes sum_{i=a}^{a+L-1} (i+1); a full one L*S; an image (GCA or Gen
+    Image) segment L*(a+L), since each of its rows sees every key before the segment end.
+    Then each Gen Image [a, a+L) is removed from the S - (a+L) rows after it: every one of
+    those rows would otherwise see all L of its keys (they all lie below the row)."""
     total = 0
     for a, L, kind in segments:
         a, L = int(a), int(L)
@@ -45,6 +47,9 @@ def closed_form_pairs(segments, S):
             total += L * S
         else:
             total += L * (a + L)
+    for a, L, kind in segments:
+        if kind == GEN:
+            total -= int(L) * (S - int(a) - int(L))
     return total
 
 
@@ -61,7 +66,9 @@ def pin_pair_counts():
 def pin_mask_elementwise_bruteforce():
     from oracle.brute import _allowed
     layouts = [[(C, 5), (F, 7), (C, 4)], [(C, 3), (G, 6), (C, 2), (G, 5), (G, 3), (C, 1)],
-               [(G, 9)], [(F, 4), (C, 6)]]
+               [(G, 9)], [(F, 4), (C, 6)],
+               [(C, 3), (GEN, 5), (C, 2), (GEN, 4), (F, 3), (C, 2)], [(GEN, 6), (C, 3)],
+               [(C, 2), (GEN, 4), (GEN, 3), (G, 3), (C, 1)], [(F, 3), (GEN, 4), (F, 2)]]
     for segs in layouts:
         w = small_workload([W.Segment(k, n) for k, n in segs])
         table = W.segment_table(w)[0]
@@ -93,6 +100,39 @@ def pin_mask_special_cases():
     assert np.array_equal(a, tril)
     b = oracle.mask.explicit_mask(np.array([[0, 20, G], [20, 17, G]]), S)
     assert not np.array_equal(b, oracle.mask.explicit_mask(np.array([[0, S, G]]), S))
+
+
+def pin_mask_gen_hole():
+    """Gen Images (multi-image training, HunyuanImage 3.0 digest, Figure 4(b)): the mask
+    differs from the plain image (GCA) mask only by holes below the diagonal, one block
+    [end, S) x [start, end) per Gen Image; its own rows see all of it; every row still
+    sees itself; and with a single Gen Image at the end of the sequence (the inference
+    case) the mask is the canonical GCA mask."""
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        S = int(rng.integers(4, 60))
+        n = int(rng.integers(1, 7))
+        cuts = sorted(rng.choice(np.arange(1, S), size=min(S - 1, n - 1), replace=False).tolist())
+        b = [0, *cuts, S]
+        t = np.array([[a, e - a, int(rng.choice([C, F, G, GEN, GEN]))] for a, e in zip(b, b[1:])])
+        M = oracle.mask.explicit_mask(t, S)
+        as_gca = t.copy()
+        as_gca[as_gca[:, 2] == GEN, 2] = G
+        M_gca = oracle.mask.explicit_mask(as_gca, S)
+        diff = M_gca & ~M
+        assert not (M & ~M_gca).any()                 # only removes pairs
+        assert not np.triu(diff).any()                # strictly below the diagonal
+        hole = np.zeros((S, S), dtype=bool)
+        for a, L, k in t:
+            if k == GEN:
+                hole[a + L:, a:a + L] = True
+                assert M[a:a + L, a:a + L].all()      # the image's own rows see it
+        assert np.array_equal(diff, hole), t.tolist()
+        assert np.diagonal(M).all()
+    t = np.array([[0, 7, C], [7, 9, G], [16, 5, C], [21, 12, GEN]])
+    g = t.copy()
+    g[3, 2] = G
+    assert np.array_equal(oracle.mask.explicit_mask(t, 33), oracle.mask.explicit_mask(g, 33))
 
 
 # ---------------------------------------------------------------- RMSNorm
@@ -284,22 +324,37 @@ def pin_bruteforce():
 # ---------------------------------------------------------------- tiles
 def closed_form_labels(segments, S, bq, bk, q_end_aligned=False):
     """Labels from per-row key limits: a causal row i sees [0, i+1), a full row [0, S),
-    an image row [0, end of its segment). Every row is a prefix, so per query block
-    tiles below floor(min lim / bk) are FULL (all of them if min lim = S), tiles from
-    ceil(max lim / bk) on are SKIP, and the rest PARTIAL. Query blocks start at row 0, or
-    at S - nq * bq (clipped at 0) when end-aligned."""
+    an image row [0, end of its segment). Without Gen Images every row is a prefix, so per
+    query block tiles below floor(min lim / bk) are FULL (all of them if min lim = S),
+    tiles from ceil(max lim / bk) on are SKIP, and the rest PARTIAL. A Gen Image's keys
+    are seen only by rows before its end (kvis = that end; S for other keys), so pair
+    (i, j) is allowed iff j < lim(i) and i < kvis(j): a tile is FULL iff every row's
+    limit covers it and every key's kvis lies past the block's last row, and SKIP when
+    no row's limit reaches it or every key's kvis is at or before the block's first row
+    (exact for these segment kinds). Query blocks start at row 0, or at S - nq * bq
+    (clipped at 0) when end-aligned."""
     lim = np.empty(S, dtype=np.int64)
+    kvis = np.full(S, S, dtype=np.int64)
     for a, L, kind in segments:
         i = np.arange(a, a + L)
         lim[a:a + L] = i + 1 if kind == C else (S if kind == F else a + L)
+        if kind == GEN:
+            kvis[a:a + L] = a + L
     nq, nk = -(-S // bq), -(-S // bk)
     q0 = S - nq * bq if q_end_aligned else 0
     out = np.empty((nq, nk), dtype=np.uint8)
     for qb in range(nq):
-        l = lim[max(q0 + qb * bq, 0):q0 + (qb + 1) * bq]
-        kfull = nk if l.min() >= S else l.min() // bk
-        kend = -(-l.max() // bk)
-        out[qb] = [1 if kb < kfull else (2 if kb < kend else 0) for kb in range(nk)]
+        r0, r1 = max(q0 + qb * bq, 0), min(q0 + (qb + 1) * bq, S)
+        l = lim[r0:r1]
+        for kb in range(nk):
+            c0, c1 = kb * bk, min((kb + 1) * bk, S)
+            kv = kvis[c0:c1]
+            if l.max() <= c0 or kv.max() <= r0:
+                out[qb, kb] = 0
+            elif l.min() >= c1 and kv.min() > r1 - 1:
+                out[qb, kb] = 1
+            else:
+                out[qb, kb] = 2
     return out
 
 
@@ -317,6 +372,18 @@ def pin_tile_labels():
             lab = oracle.tile_labels(M, 64, 64, q_end_aligned=end)
             assert [int((lab == t).sum()) for t in (0, 1, 2)] == [
                 gold[key][name]["skip"], gold[key][name]["full"], gold[key][name]["partial"]], name
+    # random layouts of every kind, Gen Images included, at several block shapes
+    rng = np.random.default_rng(12)
+    for trial in range(60):
+        S = int(rng.integers(2, 200))
+        n = int(rng.integers(1, 8))
+        cuts = sorted(rng.choice(np.arange(1, S), size=min(S - 1, n - 1), replace=False).tolist())
+        b = [0, *cuts, S]
+        t = np.array([[a, e - a, int(rng.choice([C, F, G, GEN, GEN]))] for a, e in zip(b, b[1:])])
+        M = oracle.mask.explicit_mask(t, S)
+        for bq, bk in ((64, 64), (128, 64), (16, 8), (8, 16)):
+            assert np.array_equal(oracle.tile_labels(M, bq, bk, q_end_aligned=True),
+                                  closed_form_labels(t, S, bq, bk, q_end_aligned=True)), (t.tolist(), bq)
 
 # ---------------------------------------------------------------- backward (oracle/backward.py)
 

@@ -81,6 +81,24 @@ def _mask_gca_no_segment(segments, S, rows):
     return M
 
 
+def _mask_gen_variant(strict=False, none=False, own_rows=False):
+    """Gen Image hole mistakes: rows at the image's end still see it (strict), no hole at
+    all (none), or the image hidden from its own rows too (own_rows)."""
+    def mask_rows(segments, S, rows):
+        table = np.asarray(segments)
+        as_gca = table.copy()
+        as_gca[as_gca[:, 2] == 3, 2] = 2
+        M = _orig_mask_rows(as_gca, S, rows)
+        if none:
+            return M
+        for r, i in enumerate(np.asarray(rows)):
+            for a, L, k in table:
+                if k == 3 and (i > a + L if strict else (i >= a if own_rows else i >= a + L)):
+                    M[r, a:a + L] = False
+        return M
+    return mask_rows
+
+
 _orig_mask_rows = oracle.mask.mask_rows
 _orig_attention = oracle.masked_attention.attention
 
@@ -143,6 +161,12 @@ MUTATIONS = {
                             "pin_mask_elementwise_bruteforce"]),
     "mask_gca_without_segment": ([(oracle.mask, "mask_rows", _mask_gca_no_segment)],
                                  ["pin_pair_counts", "pin_mask_special_cases"]),
+    "mask_gen_hole_off_by_one": ([(oracle.mask, "mask_rows", _mask_gen_variant(strict=True))],
+                                 ["pin_pair_counts", "pin_mask_gen_hole", "pin_mask_elementwise_bruteforce"]),
+    "mask_gen_no_hole": ([(oracle.mask, "mask_rows", _mask_gen_variant(none=True))],
+                         ["pin_pair_counts", "pin_mask_gen_hole", "pin_mask_elementwise_bruteforce"]),
+    "mask_gen_hidden_from_itself": ([(oracle.mask, "mask_rows", _mask_gen_variant(own_rows=True))],
+                                    ["pin_pair_counts", "pin_mask_gen_hole", "pin_mask_elementwise_bruteforce"]),
     "attn_dropped_scale": ([(oracle.masked_attention, "attention", _attn_no_scale)],
                            ["pin_attention_library"]),
     "attn_k_used_as_v": ([(oracle.masked_attention, "attention", _attn_k_for_v)],

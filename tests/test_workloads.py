@@ -32,7 +32,8 @@ def test_hunyuan_grid():
 
 
 def test_config_sizes():
-    want = {"tiny": 80, "hd1024": 1282, "hd2048": 4354, "edit": 8448, "hunyuan": 6016}
+    want = {"tiny": 80, "hd1024": 1282, "hd2048": 4354, "edit": 8448, "hunyuan": 6016,
+            "hunyuan_multigen": 6016}
     assert {n: c.seq_len for n, c in W.CONFIGS.items()} == want
 
 

@@ -10,6 +10,9 @@ Segment kinds (the per-token segment type of the unified sequence):
   SEG_GCA     HunyuanImage 3.0 image segment: rows attend to everything before them
               plus every token of their own segment (HunyuanImage 3.0 digest,
               "Generalized Causal Attention", the core rule).
+  SEG_GEN     HunyuanImage 3.0 Gen Image of a multi-image training sequence: rows as
+              SEG_GCA, and no token after the segment attends to it (same digest,
+              "Generalized Causal Attention", the multi-generation training paragraph).
 
 Shapes: HiDream-O1 uses 32x32-pixel patches, so a 1024^2 image is a 32x32 grid and
 2048^2 is 64x64, behind a chat-template prefix that ends in the two markers
@@ -28,6 +31,7 @@ from typing import Optional, Tuple
 SEG_CAUSAL = 0
 SEG_FULL = 1
 SEG_GCA = 2
+SEG_GEN = 3
 
 ROPE_NONE = "none"
 ROPE_1D = "1d"
@@ -85,7 +89,7 @@ def _hd(name, desc, batch, segs, seed, **kw):
                     **base)
 
 
-C, F, G = SEG_CAUSAL, SEG_FULL, SEG_GCA
+C, F, G, GEN = SEG_CAUSAL, SEG_FULL, SEG_GCA, SEG_GEN
 
 CONFIGS = {
     "tiny": Workload(
@@ -115,6 +119,17 @@ CONFIGS = {
                   Segment(G, 4096, (64, 64)), Segment(C, 128)),
         n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", rope=ROPE_2D,
         rope_theta=1e4, qk_norm=False, seed=4),
+    "hunyuan_multigen": Workload(
+        name="hunyuan_multigen",
+        description="HunyuanImage-style multi-image training sequence: B=1, [512 text]"
+                    "[1024 Gen Image 32x32][256 text][4096 Gen Image 64x64][128 text], every "
+                    "Gen Image hidden from the tokens after it, GQA 32/8, d=128, bf16, 2D RoPE "
+                    "on images, 1D on text, theta 1e4",
+        batch=1,
+        segments=(Segment(C, 512), Segment(GEN, 1024, (32, 32)), Segment(C, 256),
+                  Segment(GEN, 4096, (64, 64)), Segment(C, 128)),
+        n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", rope=ROPE_2D,
+        rope_theta=1e4, qk_norm=False, seed=6),
 }
 
 
