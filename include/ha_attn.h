@@ -12,6 +12,10 @@
  *   HA_SEG_GCA     HunyuanImage 3.0 image tokens: keys j <= i plus every key of their own
  *                  image segment (HunyuanImage 3.0 digest, "Generalized Causal Attention",
  *                  the core rule)
+ *   HA_SEG_GEN     a Gen Image of a multi-image HunyuanImage 3.0 training sequence: its
+ *                  rows as HA_SEG_GCA, and no token after the segment attends to it, which
+ *                  leaves a hole below the diagonal (same digest and section, the
+ *                  multi-generation training paragraph and Figure 4(b))
  * Scores use GQA (consecutive groups of n_q_heads / n_kv_heads query heads share one KV
  * head), optional q/k RMSNorm and 1D / generalized 2D / 3-axis interleaved rotary
  * embeddings (hidream-o1-p100a model card, architecture paragraph; HunyuanImage 3.0
@@ -44,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 2
+#define HA_ABI_VERSION 3
 #define HA_MAX_SEGMENTS 64      /* segments per batch item */
 #define HA_MAX_SEQ_LEN (1 << 22)
 
@@ -58,14 +62,14 @@ typedef enum {
   HA_ERR_HIP = 6            /* a HIP launch or runtime call failed */
 } ha_status;
 
-typedef enum { HA_SEG_CAUSAL = 0, HA_SEG_FULL = 1, HA_SEG_GCA = 2 } ha_seg_kind;
+typedef enum { HA_SEG_CAUSAL = 0, HA_SEG_FULL = 1, HA_SEG_GCA = 2, HA_SEG_GEN = 3 } ha_seg_kind;
 typedef enum { HA_DTYPE_BF16 = 0, HA_DTYPE_F32 = 1 } ha_dtype;
 typedef enum { HA_ROPE_NONE = 0, HA_ROPE_1D = 1, HA_ROPE_2D = 2, HA_ROPE_MROPE = 3 } ha_rope_kind;
 typedef enum { HA_TILE_SKIP = 0, HA_TILE_FULL = 1, HA_TILE_PARTIAL = 2 } ha_tile_label;
 
 /* One segment of one batch item: tokens [start, start + length) of kind ha_seg_kind.
  * A batch item's segments must be listed in order, contiguous from 0, with positive
- * lengths summing to seq_len. Adjacent HA_SEG_GCA segments are distinct images. */
+ * lengths summing to seq_len. Adjacent image segments are distinct images. */
 typedef struct {
   int32_t start;
   int32_t length;
@@ -134,12 +138,15 @@ ha_status ha_tile_shape(const ha_attn_desc* desc, int32_t* block_q, int32_t* blo
                         int32_t* n_q_blocks, int32_t* n_k_blocks);
 
 /* Segment-table tile classifier. Every query row i may attend to a key prefix
- * [0, lim(i)): causal rows lim = i + 1, full rows lim = seq_len, image (GCA) rows
- * lim = end of their segment. Writes, on the stream:
- *   row_limit [batch][seq_len] int32        lim(i)                      (may be NULL)
- *   ranges    [batch][n_q_blocks][2] int32  (kfull, kend): tiles [0, kfull) are FULL,
+ * [0, lim(i)): causal rows lim = i + 1, full rows lim = seq_len, image (GCA and Gen)
+ * rows lim = end of their segment; Gen Images then cut holes into the prefixes of the
+ * rows after them. Writes, on the stream:
+ *   row_limit [batch][seq_len] int32        lim(i), before any hole      (may be NULL)
+ *   ranges    [batch][n_q_blocks][2] int32  (kfull, kend) from the row limits: without
+ *                                           Gen Images tiles [0, kfull) are FULL,
  *                                           [kfull, kend) PARTIAL, the rest SKIP
- *   labels    [batch][n_q_blocks][n_k_blocks] uint8 ha_tile_label       (may be NULL)
+ *   labels    [batch][n_q_blocks][n_k_blocks] uint8 ha_tile_label, holes included
+ *                                                                         (may be NULL)
  * Tiles follow ha_tile_shape's grid (query blocks end-aligned).
  * Over the valid part of a tile (rows and keys in [0, seq_len)): SKIP = no allowed pair,
  * FULL = all allowed, PARTIAL = otherwise. All DEVICE pointers, 4-byte aligned
@@ -154,14 +161,18 @@ ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
                          void* stream);
 
 /* Workspace bytes ha_attn_fwd needs: row limits, tile ranges, and the rotated q and k
- * when pro is not NULL. */
+ * when pro is not NULL; with HA_SEG_GEN segments also per-key visibility and per query
+ * block tile lists. */
 size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro);
 
 /* Attention on prepared inputs: q and k already normalised and rotated (q optionally
  * prescaled, see ha_attn_desc.q_prescaled), row_limit and ranges from ha_classify_tiles
  * for the same descriptor (so the tile plan can be reused across layers and denoising
  * steps). out = softmax(scale * q k^T, masked) v per query head, fp32 accumulation, P
- * rounded to the input dtype for the second product. */
+ * rounded to the input dtype for the second product. Layouts with HA_SEG_GEN segments
+ * need more of the plan than row_limit and ranges: they return HA_ERR_UNSUPPORTED here
+ * (and in ha_attn_fwd_planned_from); ha_attn_fwd, ha_attn_fwd_lse and ha_attn_bwd take
+ * them. */
 ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const void* k,
                               const void* v, const int32_t* row_limit, const int32_t* ranges,
                               void* out, void* stream);
@@ -211,8 +222,9 @@ ha_status ha_attn_fwd_lse(const ha_attn_desc* desc, const ha_prologue_desc* pro,
                           size_t workspace_bytes, void* stream);
 
 /* Workspace bytes ha_attn_bwd needs: row limits, tile ranges, the rebuilt prologue
- * outputs, per-row dout . out, fp32 gradients of the rotated q and k, and with RMSNorm
- * per-token weight-gradient partials. */
+ * outputs, per-row dout . out, fp32 gradients of the rotated q and k, with RMSNorm
+ * per-token weight-gradient partials, and with HA_SEG_GEN segments the key visibility and
+ * tile lists. */
 size_t ha_attn_bwd_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro);
 
 /* Gradients for the output gradient dout (same layout as out): dq, dk, dv with respect

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     assert len(names) == 15 and sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
-    assert U.ha_abi_version() == 2
+    assert U.ha_abi_version() == 3
 
 
 def seg(rows, batch=1):
@@ -257,3 +257,21 @@ def test_prefix_entry_points_check_ranges():
     U.ha_attn_fwd_planned_from(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 80, stream=0)
     U.ha_qk_prologue_from(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, 80, stream=0)
     assert U.ha_last_error() == ""
+
+
+def test_gen_image_layouts():
+    """Gen Image segments (kind 3) are accepted; the planned calls, which lack the hole
+    plan, refuse them before any launch; the workspaces grow by the plan arrays."""
+    g = seg([[0, 16, 0], [16, 32, 3], [48, 32, 0]])
+    d = desc(segments=g)
+    for call in (lambda: U.ha_attn_fwd_planned(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
+                 lambda: U.ha_attn_fwd_planned_from(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, stream=0)):
+        with pytest.raises(U.HAError) as e:
+            call()
+        assert e.value.status == B.HA_ERR_UNSUPPORTED and "Gen Image" in str(e.value)
+    plain = desc(segments=seg([[0, 16, 0], [16, 32, 2], [48, 32, 0]]))
+    _, _, nq, nk = U.ha_tile_shape(d)
+    extra = 256 * 4 + nq * nk * 4 + nq * 2 * 4   # key visibility (rows padded to 256), lists, counts
+    assert U.ha_attn_workspace_bytes(d) - U.ha_attn_workspace_bytes(plain) >= extra
+    bd, bp = bf16_desc(segments=g), bf16_desc(segments=seg([[0, 16, 0], [16, 32, 2], [48, 32, 0]]))
+    assert U.ha_attn_bwd_workspace_bytes(bd) - U.ha_attn_bwd_workspace_bytes(bp) >= extra

@@ -32,7 +32,7 @@ from workloads.device import to_device
 
 pytestmark = pytest.mark.gpu
 
-C, F, G = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA
+C, F, G, GEN = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA, W.SEG_GEN
 GRAD_ROW, GRAD_ROW_BULK, GRAD_MEAN, ROW_FLOOR, LSE_ABS = 5e-2, 1e-2, 1e-2, 0.5, 2e-2
 
 
@@ -65,6 +65,17 @@ SMALL = {
     "all_full": small([W.Segment(F, 200)], rope="2d", theta=1e4),
     "no_prologue": small([W.Segment(C, 37), W.Segment(F, 64, (8, 8))], rope="none", norm=False),
     "rows_before_keys_of_block": small([W.Segment(C, 3), W.Segment(F, 130)], hq=4, hkv=1),
+    # Gen Images of a multi-image training sequence: hidden from every token after them
+    "gen_small": small([W.Segment(C, 33), W.Segment(GEN, 64, (8, 8)), W.Segment(C, 17),
+                        W.Segment(GEN, 100, (10, 10)), W.Segment(C, 5)], rope="2d", norm=False, theta=1e4),
+    "gen_first": small([W.Segment(GEN, 81, (9, 9)), W.Segment(C, 100)], rope="2d", theta=1e4),
+    "gen_adjacent_g2": small([W.Segment(C, 20), W.Segment(GEN, 49, (7, 7)), W.Segment(GEN, 36, (6, 6)),
+                              W.Segment(G, 25, (5, 5)), W.Segment(C, 70)], hq=4, hkv=2),
+    "gen_g1_d64": small([W.Segment(C, 40), W.Segment(GEN, 64, (8, 8)), W.Segment(F, 30), W.Segment(C, 60)],
+                        hq=2, hkv=2, d=64),
+    "gen_long": small([W.Segment(C, 130), W.Segment(GEN, 256, (16, 16)), W.Segment(C, 70),
+                       W.Segment(GEN, 400, (20, 20)), W.Segment(C, 40)], rope="2d", norm=False, theta=1e4,
+                      batch=1),
 }
 
 
@@ -170,6 +181,22 @@ def test_backward_hd2048_one_group():
     check("hd2048 dq", got["dq"][1, :, heads], want["dq"][0, :, heads])
     check("hd2048 dk", got["dk"][1, :, 3], want["dk"][0, :, 3])
     check("hd2048 dv", got["dv"][1, :, 3], want["dv"][0, :, 3])
+
+
+def test_backward_multigen_one_group():
+    """The multi-image training layout at full size (text, a 32x32 Gen Image, text, a
+    64x64 Gen Image, text; S = 6016); the oracle computes KV group 5 (its 4 query heads'
+    dq, its dk and dv)."""
+    w = W.get_config("hunyuan_multigen")
+    print("case hunyuan_multigen: group 5", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w, seed=80)
+    got = run_train(x, dout)
+    want = oracle.path_backward(x, dout, groups=[5])
+    heads = slice(20, 24)
+    check("multigen dq", got["dq"][0, :, heads], want["dq"][0, :, heads])
+    check("multigen dk", got["dk"][0, :, 5], want["dk"][0, :, 5])
+    check("multigen dv", got["dv"][0, :, 5], want["dv"][0, :, 5])
 
 
 def test_autograd_matches_direct_calls():

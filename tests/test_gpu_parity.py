@@ -16,7 +16,7 @@ from workloads.device import to_device
 
 pytestmark = pytest.mark.gpu
 
-C, F, G = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA
+C, F, G, GEN = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA, W.SEG_GEN
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,6 +58,22 @@ SMALL = {
                        dtype="f32", hq=4, hkv=1, d=64, rope="2d", theta=1e4),
     "f32_d128": small([W.Segment(C, 30), W.Segment(F, 70)], dtype="f32", hq=8, hkv=2, d=128,
                       rope="mrope"),
+    # Gen Images (multi-image training): each hidden from every token after it
+    "gen_small": small([W.Segment(C, 33), W.Segment(GEN, 64, (8, 8)), W.Segment(C, 17),
+                        W.Segment(GEN, 100, (10, 10)), W.Segment(C, 5)], rope="2d", norm=False,
+                       theta=1e4),
+    "gen_adjacent": small([W.Segment(C, 20), W.Segment(GEN, 49, (7, 7)), W.Segment(GEN, 36, (6, 6)),
+                           W.Segment(G, 25, (5, 5)), W.Segment(C, 70)]),
+    # the first key tiles hidden from every later row (rows whose first listed tiles are empty)
+    "gen_first": small([W.Segment(GEN, 81, (9, 9)), W.Segment(C, 100)], rope="2d", theta=1e4),
+    "gen_then_full": small([W.Segment(C, 10), W.Segment(GEN, 64, (8, 8)), W.Segment(F, 64, (8, 8)),
+                            W.Segment(C, 30)]),
+    "gen_g8": small([W.Segment(C, 40), W.Segment(GEN, 64, (8, 8)), W.Segment(C, 100)], hq=16, hkv=2,
+                    rope="none"),
+    "gen_g1_d64": small([W.Segment(C, 40), W.Segment(GEN, 64, (8, 8)), W.Segment(C, 60)], hq=2, hkv=2,
+                        d=64),
+    "f32_gen": small([W.Segment(C, 20), W.Segment(GEN, 36, (6, 6)), W.Segment(C, 25)], dtype="f32",
+                     hq=4, hkv=1, d=64, rope="2d", theta=1e4),
 }
 
 
@@ -74,14 +90,21 @@ def classify(w, segments=None):
 
 
 def check_labels(w, segments):
+    """Labels against the oracle's brute force over the mask (Gen Image holes included);
+    row limits and ranges describe the key prefixes before any hole, i.e. those of the same
+    layout with every Gen Image as a plain image segment."""
     (bq, bk), labels, ranges, lim = classify(w, segments)
     for b in range(w.batch):
         M = oracle.explicit_mask(segments[b], w.seq_len)
         want = oracle.tile_labels(M, bq, bk, q_end_aligned=True)
         assert np.array_equal(labels[b], want), f"batch {b}: tile labels differ"
-        assert np.array_equal(lim[b], M.sum(axis=1)), f"batch {b}: row limits differ"
-        kfull = (want == 1).sum(axis=1)
-        kend = want.shape[1] - (want == 0).sum(axis=1)
+        pre = np.array(segments[b])
+        pre[pre[:, 2] == GEN, 2] = G
+        Mp = oracle.explicit_mask(pre, w.seq_len)
+        assert np.array_equal(lim[b], Mp.sum(axis=1)), f"batch {b}: row limits differ"
+        wp = oracle.tile_labels(Mp, bq, bk, q_end_aligned=True)
+        kfull = (wp == 1).sum(axis=1)
+        kend = wp.shape[1] - (wp == 0).sum(axis=1)
         assert np.array_equal(ranges[b, :, 0], kfull) and np.array_equal(ranges[b, :, 1], kend)
 
 
@@ -101,7 +124,7 @@ def test_classifier_bit_exact_random_layouts():
         for b in range(batch):
             cuts = np.sort(rng.choice(np.arange(1, S), size=n - 1, replace=False)) if n > 1 else []
             bounds = [0, *cuts, S]
-            kinds = rng.integers(0, 3, size=n)
+            kinds = rng.integers(0, 4, size=n)  # Gen Images included
             tables.append([[bounds[s], bounds[s + 1] - bounds[s], kinds[s]] for s in range(n)])
         seg = np.array(tables, dtype=np.int32)
         w = small([W.Segment(C, S)], batch=batch, hq=[8, 4, 16, 2][trial % 4], hkv=2)
@@ -168,7 +191,7 @@ def test_tiny_config_fp32():
     compare(f64(out), oracle.hot_path(x), "f32", "tiny")
 
 
-@pytest.mark.parametrize("name", ["hd1024", "hd2048", "edit", "hunyuan"])
+@pytest.mark.parametrize("name", ["hd1024", "hd2048", "edit", "hunyuan", "hunyuan_multigen"])
 def test_full_size_sampled_rows(name):
     w = W.get_config(name)
     x = W.generate(w)
@@ -202,19 +225,19 @@ def test_long_sequence_sampled_rows():
     compare(got[0, rows][:, heads], want, w.dtype, f"hd4096 ({len(rows)} rows x {len(heads)} heads)")
 
 
-def test_max_segment_count():
+@pytest.mark.parametrize("kinds", [[C, F, G], [C, F, G, GEN]], ids=["plain", "gen"])
+def test_max_segment_count(kinds):
     """64 segments per item (the most a table may hold), random kinds and lengths, image
     segments side by side, two items with different tables: whole output against the
     oracle."""
     rng = np.random.default_rng(11)
-    kinds = [C, F, G]
     S = 700
     segs = []
     for b in range(2):
         lens = rng.integers(1, 11, size=64)
         lens[-1] += S - lens.sum()
         at, rows = 0, []
-        for L, k in zip(lens, rng.integers(0, 3, size=64)):
+        for L, k in zip(lens, rng.integers(0, len(kinds), size=64)):
             rows.append([at, int(L), kinds[int(k)]])
             at += int(L)
         segs.append(rows)
@@ -249,7 +272,7 @@ def test_careful_pass_full_size_shape():
 def uniform_probe(w):
     """q = 0 makes every allowed weight exactly 1 (RMSNorm and rotary of 0 are 0), masked
     ones exactly 0; with v_j one-hot on channel (j // 64) mod d the output channel c of row
-    i is the count of allowed keys in the 64-key blocks on c, over lim(i)."""
+    i is the count of allowed keys in the 64-key blocks on c, over the row's allowed keys."""
     x = W.generate(w)
     x.q[:] = 0.0
     S, d = w.seq_len, w.head_dim
@@ -259,19 +282,21 @@ def uniform_probe(w):
     out, _ = run_fwd(refresh_bits(x))
     got = f64(out)
     for b in range(w.batch):
-        lim = oracle.explicit_mask(x.segments[b], S).sum(axis=1)
+        M = oracle.explicit_mask(x.segments[b], S)
         for i in np.unique(np.r_[np.arange(0, S, 7), S - 1]):
-            want = np.bincount(chan[:lim[i]], minlength=d) / lim[i]
+            keys = np.nonzero(M[i])[0]
+            want = np.bincount(chan[keys], minlength=d) / len(keys)
             tol = 2.0 ** -7 * want + 1e-7
             assert (np.abs(got[b, i] - want[None, :]) <= tol).all(), (w.name, b, i)
 
 
-@pytest.mark.parametrize("name", ["hd2048", "edit", "hunyuan"])
+@pytest.mark.parametrize("name", ["hd2048", "edit", "hunyuan", "hunyuan_multigen"])
 def test_uniform_probe_full_size(name):
     uniform_probe(W.get_config(name))
 
 
-@pytest.mark.parametrize("name", ["hd_small", "edit_small", "gca_small", "all_full"])
+@pytest.mark.parametrize("name", ["hd_small", "edit_small", "gca_small", "all_full", "gen_small",
+                                  "gen_first", "f32_gen"])
 def test_uniform_probe_small(name):
     uniform_probe(SMALL[name])
 
@@ -289,6 +314,22 @@ def test_future_tokens_do_not_leak():
     b0, p0 = base.cpu(), pert.cpu()
     assert torch.equal(b0[0, :97], p0[0, :97])          # rows that end before token 120
     assert not torch.equal(b0[0, 97:120], p0[0, 97:120])  # image rows see their whole segment
+
+
+def test_gen_image_hidden_from_later_rows():
+    """Rows after a Gen Image do not depend on its tokens; its own rows do."""
+    w = SMALL["gen_small"].replace(batch=1)
+    x = W.generate(w)
+    base, _ = run_fwd(x)
+    # segments: C[0,33) GEN[33,97) C[97,114) GEN[114,214) C[214,219)
+    y = W.generate(w)
+    y.k[0, 33:97] += 1.0
+    y.v[0, 33:97] += 1.0
+    pert, _ = run_fwd(refresh_bits(y))
+    b0, p0 = base.cpu(), pert.cpu()
+    assert torch.equal(b0[0, :33], p0[0, :33])            # before it
+    assert torch.equal(b0[0, 97:], p0[0, 97:])            # everything after it
+    assert not torch.equal(b0[0, 33:97], p0[0, 33:97])    # its own rows
 
 
 def planned(x, dev, prescaled):

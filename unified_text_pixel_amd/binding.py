@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libha.so")
 
 HA_OK, HA_ERR_INVALID_ARG, HA_ERR_UNSUPPORTED, HA_ERR_SEGMENTS = 0, 1, 2, 3
 HA_ERR_ALIGNMENT, HA_ERR_WORKSPACE, HA_ERR_HIP = 4, 5, 6
-HA_SEG_CAUSAL, HA_SEG_FULL, HA_SEG_GCA = 0, 1, 2
+HA_SEG_CAUSAL, HA_SEG_FULL, HA_SEG_GCA, HA_SEG_GEN = 0, 1, 2, 3
 HA_DTYPE_BF16, HA_DTYPE_F32 = 0, 1
 HA_ROPE_NONE, HA_ROPE_1D, HA_ROPE_2D, HA_ROPE_MROPE = 0, 1, 2, 3
 HA_TILE_SKIP, HA_TILE_FULL, HA_TILE_PARTIAL = 0, 1, 2

@@ -39,6 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -141,7 +142,11 @@ struct CfgKV {
   static constexpr int SUB = 8 / G;               // 32-row steps per query block
 };
 
-template <int D, int G>
+// HOLE: a layout with Gen Images. Each lane's key carries its visibility (the rows below
+// it see the key), and the block's smallest and largest visibility bound the steps: rows
+// at or after the largest see none of the block's keys, rows at or after the smallest need
+// the per-pair mask.
+template <int D, int G, bool HOLE>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   using C = CfgKV<D, G>;
   __shared__ __attribute__((aligned(1024))) char kt[C::KVBYTES];
@@ -165,6 +170,32 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   const int BQ = 32 * C::SUB;          // rows of a forward query block
   const int qrow0 = S - nq * BQ;       // first row of query block 0 (end-aligned blocks)
 
+  // Gen Images: the lane key's visibility, and its range over the block's keys inside the
+  // sequence (every wave reduces all of them, so the bounds are uniform without LDS;
+  // loaded before any DMA is issued, so using them waits for nothing else)
+  int kv = S, kvmin = S, kvmax = S;
+  if constexpr (HOLE) {
+    const int32_t* kvb = a.key_vis + (int64_t)b * a.kv_stride;
+    kv = kvb[key];  // key < key_vis_stride(S): blocks of KB keys tile it
+    int lo = S, hi_ = 0;
+#pragma unroll
+    for (int j = 0; j < C::KB / 64; ++j) {
+      const int kj = k0 + 64 * j + lane;
+      const int v = kvb[kj];
+      if (kj < S) {
+        lo = min(lo, v);
+        hi_ = max(hi_, v);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      lo = min(lo, __shfl_xor(lo, m));
+      hi_ = max(hi_, __shfl_xor(hi_, m));
+    }
+    kvmin = __builtin_amdgcn_readfirstlane(lo);
+    kvmax = __builtin_amdgcn_readfirstlane(hi_);
+  }
+
   // the item's K and V rows
   const int64_t kvstride = (int64_t)a.Hkv * D * 2;
   const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * S * a.Hkv + g) * D * 2;
@@ -182,6 +213,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   auto next_step = [&](int s) __attribute__((always_inline)) {
     for (++s; s < nsteps; ++s) {
       if (qrow0 + 32 * s + 31 < 0) continue;
+      if (HOLE && qrow0 + 32 * s >= kvmax) return -1;  // this and later rows see no key here
       const int qb = s / C::SUB;
       if (a.ranges[((int64_t)b * nq + qb) * 2 + 1] * BK > k0) return s;
       s = (qb + 1) * C::SUB - 1;
@@ -215,7 +247,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   auto masked_step = [&](int s) __attribute__((always_inline)) {
     const int qb = s / C::SUB;
     const int kfull = a.ranges[((int64_t)b * nq + qb) * 2 + 0];
-    return !(qrow0 + 32 * s >= 0 && k0 + C::KB <= kfull * BK && k0 + C::KB <= S);
+    return !(qrow0 + 32 * s >= 0 && k0 + C::KB <= kfull * BK && k0 + C::KB <= S) ||
+           (HOLE && qrow0 + 32 * s + 31 >= kvmin);
   };
 
   // A/B operand reads of rows (q' or dO row ln, or K/V row 32 ksl + ln): chunk 2kk + hi of
@@ -275,7 +308,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
       if (masked) {
         const int src = 8 * (r >> 2) + 4 * hi + (r & 3);
         const int lim = __builtin_bit_cast(int, bpermute(src, __builtin_bit_cast(float, mr)));
-        p = key < lim ? p : 0.f;
+        p = (key < lim && (!HOLE || qrow0 + 32 * s + src < kv)) ? p : 0.f;
       }
       pa[r >> 3][r & 7] = static_cast<__bf16>(p);
       za[r >> 3][r & 7] = static_cast<__bf16>(p * pacc[r]);
@@ -398,7 +431,10 @@ struct CfgQ {
   static constexpr int TBYTES = BK * D * 2;
 };
 
-template <int D, int G>
+// HOLE: a layout with Gen Images; the block walks its tile list (positions below the
+// count of inside FULL tiles need no mask) and masked tiles also hide keys whose
+// visibility ends at or before the row.
+template <int D, int G, bool HOLE>
 __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
   using C = CfgQ<D, G>;
   __shared__ __attribute__((aligned(1024))) char k0[C::TBYTES];
@@ -419,15 +455,24 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
   const bool row_ok = i >= 0;
   const int ic = row_ok ? i : 0;
   const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : 0;
-  const int kend = a.ranges[((int64_t)b * nq + qb) * 2 + 1];
+  const int32_t* cnt = HOLE ? a.tile_count : a.ranges;
+  const int kfull = HOLE ? cnt[((int64_t)b * nq + qb) * 2 + 0] : 0;
+  const int kend = cnt[((int64_t)b * nq + qb) * 2 + 1];
+  const int32_t* tlist = HOLE ? a.tiles + ((int64_t)b * nq + qb) * a.nk : nullptr;
+  auto tile_at = [&](int t) __attribute__((always_inline)) {
+    if constexpr (HOLE)
+      return tlist[t];
+    else
+      return t;
+  };
 
   const int64_t kvstride = (int64_t)a.Hkv * D * 2;
   const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * S * a.Hkv + g) * D * 2;
   const char* vbase = static_cast<const char*>(a.v) + ((int64_t)b * S * a.Hkv + g) * D * 2;
   RowDma<D, 2 * D, C::TBYTES / 1024> kvd;
   kvd.init(lane);
-  kvd.issue(kbase, kvstride, 0, S - 1, k0, wave);
-  kvd.issue(vbase, kvstride, 0, S - 1, v0, wave);
+  kvd.issue(kbase, kvstride, tile_at(0) * BK, S - 1, k0, wave);
+  kvd.issue(vbase, kvstride, tile_at(0) * BK, S - 1, v0, wave);
 
   // the row's q' and dO as B operands (dims 16kk + 8hi .. +8), its log2(e) lse and delta
   bf16x8 qf[D / 16], of[D / 16];
@@ -454,9 +499,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
     wait_vm();
     __syncthreads();
     if (t + 1 < kend) {
-      kvd.issue(kbase, kvstride, (t + 1) * BK, S - 1, kn, wave);
-      kvd.issue(vbase, kvstride, (t + 1) * BK, S - 1, vn, wave);
+      kvd.issue(kbase, kvstride, tile_at(t + 1) * BK, S - 1, kn, wave);
+      kvd.issue(vbase, kvstride, tile_at(t + 1) * BK, S - 1, vn, wave);
     }
+    const int tile = tile_at(t);
     // LDS addresses from an opaque copy of the lane id, rebuilt each step (kept live
     // across the loop they would not fit in registers)
     int lo = lane;
@@ -478,10 +524,20 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
         st = mfma(*reinterpret_cast<const bf16x8*>(kr + off), qf[kk], st);
         pt = mfma(*reinterpret_cast<const bf16x8*>(vr + off), of[kk], pt);
       }
+      // Gen Images: the visibility of the lane's keys (runs of 4; key_vis rows are padded)
+      i32x4 vis[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) vis[q4] = i32x4{S, S, S, S};
+      if (HOLE && t >= kfull) {
+        const int* kvp = a.key_vis + (int64_t)b * a.kv_stride + tile * BK + 32 * kt + 4 * hix;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) vis[q4] = *reinterpret_cast<const i32x4*>(kvp + 8 * q4);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = t * BK + 32 * kt + 8 * (r >> 2) + 4 * hix + (r & 3);
-        const float p = key < lim ? __builtin_amdgcn_exp2f(st[r] - l2) : 0.f;
+        const int key = tile * BK + 32 * kt + 8 * (r >> 2) + 4 * hix + (r & 3);
+        const bool ok = key < lim && (!HOLE || i < vis[r >> 2][r & 3]);
+        const float p = ok ? __builtin_amdgcn_exp2f(st[r] - l2) : 0.f;
         zf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pt[r] - de));
       }
     }
@@ -531,13 +587,21 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
 template <int D, int G>
 hipError_t launch_kv(const BwdArgs& a, hipStream_t stream) {
   const int64_t nkb = (a.S + CfgKV<D, G>::KB - 1) / CfgKV<D, G>::KB;
-  hipLaunchKernelGGL((bwd_dkdv<D, G>), dim3((unsigned)((int64_t)a.B * a.Hkv * nkb)), dim3(512), 0, stream, a);
+  const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * nkb));
+  if (a.key_vis)
+    hipLaunchKernelGGL((bwd_dkdv<D, G, true>), grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv<D, G, false>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int G>
 hipError_t launch_q(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dq<D, G>), dim3((unsigned)((int64_t)a.B * a.Hkv * a.nq)), dim3(512), 0, stream, a);
+  const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * a.nq));
+  if (a.tiles)
+    hipLaunchKernelGGL((bwd_dq<D, G, true>), grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dq<D, G, false>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

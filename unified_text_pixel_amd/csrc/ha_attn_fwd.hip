@@ -44,6 +44,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -200,7 +201,10 @@ struct Dma {
   }
 };
 
-template <int D, int G, bool PRE, bool LSE>
+// HOLE: a layout with Gen Images. The work item walks its query block's tile list
+// (inside FULL tiles first, then the rest) instead of tiles [0, kend), and masked tiles
+// also hide keys whose visibility ends at or before the row.
+template <int D, int G, bool PRE, bool LSE, bool HOLE>
 __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   using C = CfgB<D, G>;
   using TL = Tile<D>;
@@ -225,8 +229,18 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   const bool row_ok = i >= 0;
   const int ic = row_ok ? i : 0;
   const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : S;
-  const int kfull = a.ranges[((int64_t)b * a.nq + qb) * 2 + 0];
-  const int kend = a.ranges[((int64_t)b * a.nq + qb) * 2 + 1];
+  // positions [0, kfull) of the walk are unmasked, [kfull, kend) masked; position t is
+  // key tile tile_at(t)
+  const int32_t* cnt = HOLE ? a.tile_count : a.ranges;
+  const int kfull = cnt[((int64_t)b * a.nq + qb) * 2 + 0];
+  const int kend = cnt[((int64_t)b * a.nq + qb) * 2 + 1];
+  const int32_t* tlist = HOLE ? a.tiles + ((int64_t)b * a.nq + qb) * a.nk : nullptr;
+  auto tile_at = [&](int t) __attribute__((always_inline)) {
+    if constexpr (HOLE)
+      return tlist[t];
+    else
+      return t;
+  };
   const float c = a.scale_log2e;
   Dma<D, G> dma;
   dma.init(a.k, a.v, b, g, S, a.Hkv, wave, lane);
@@ -276,16 +290,35 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     return s;
   };
 
-  // Masks tile t of S (keys >= lim) where the tile is partial or runs past the end.
+  // Masks the tile at position t of S (keys >= lim, and with Gen Images keys whose
+  // visibility ends at or before row i) where the tile is partial or runs past the end.
   auto mask = [&](f32x16 (&sc)[2], int t) {
-    if (t < kfull && (t + 1) * BK <= S) return;
+    const int tile = tile_at(t);
+    if (t < kfull && (tile + 1) * BK <= S) return;
+    if constexpr (HOLE) {
+      // the lane's keys come in runs of 4: key_vis rows are padded, so every run is in bounds
+      const int* kv = a.key_vis + (int64_t)b * a.kv_stride + tile * BK + 4 * hi;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        sc[kt][r] = key >= lim ? -INFINITY : sc[kt][r];
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const i32x4 vis = *reinterpret_cast<const i32x4*>(kv + 32 * kt + 8 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            const int key = tile * BK + 32 * kt + 8 * q4 + 4 * hi + e;
+            sc[kt][r] = (key >= lim || i >= vis[e]) ? -INFINITY : sc[kt][r];
+          }
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = tile * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
+          sc[kt][r] = key >= lim ? -INFINITY : sc[kt][r];
+        }
+    }
   };
 
   // O^T += V^T P^T for one tile; the A operand of K step KS, dims 32mt.. comes from two
@@ -319,8 +352,8 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     const char* const vr = PAR ? v0 : v1;  // V_{t-1}
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (FAST || t + 2 < kend) dma.template tile<false, !FAST>((t + 2) * BK, kw);
-    dma.template tile<true, !FAST>(t * BK, vw);
+    if (FAST || t + 2 < kend) dma.template tile<false, !FAST>(tile_at(t + 2) * BK, kw);
+    dma.template tile<true, !FAST>(tile_at(t) * BK, vw);
     if (FAST || t + 1 < kend) {
       const auto s1 = qk(kr, f32x16{});
       sn[0] = s1[0];
@@ -337,8 +370,8 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
 
   if (tid == 0) redo = 0;
   // prologue: K0 and K1 in flight, S_0 (the barrier also publishes redo = 0)
-  dma.template tile<false, true>(0, k0);
-  if (kend > 1) dma.template tile<false, true>(BK, k1);
+  dma.template tile<false, true>(tile_at(0) * BK, k0);
+  if (kend > 1) dma.template tile<false, true>(tile_at(1) * BK, k1);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // P_t sits in register set t mod 2 (pa, pb)
@@ -352,8 +385,9 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
 
   // tiles [1, fast_end) take the FAST step: tile t is full and inside the sequence, and
   // so is tile t + 2 (DMA without clamping). Both loops take two steps per trip (odd t,
-  // then even), the S registers alternating roles; sb holds S_t when a trip starts.
-  const int fast_end = max(1, min(min(kfull, kend - 2), S / BK - 2));
+  // then even), the S registers alternating roles; sb holds S_t when a trip starts. (A
+  // tile list puts the tiles that are full and inside the sequence first.)
+  const int fast_end = HOLE ? max(1, min(kfull, kend) - 2) : max(1, min(min(kfull, kend - 2), S / BK - 2));
   step(std::false_type{}, P0{}, 0, sa, sb, pb, pa);  // S_1 -> sb, P_0 -> pa
   int t = 1;
   for (; t + 1 < fast_end; t += 2) {
@@ -389,8 +423,8 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
     for (int u = 0; u < kend; ++u) {
       __syncthreads();  // every wave is done with the buffers
-      dma.template tile<false, true>(u * BK, k0);
-      dma.template tile<true, true>(u * BK, v0);
+      dma.template tile<false, true>(tile_at(u) * BK, k0);
+      dma.template tile<true, true>(tile_at(u) * BK, v0);
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       const auto s0 = qk(k0, negm);
@@ -479,8 +513,12 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
   const bool row_ok = i >= 0;
   const int ic = row_ok ? i : 0;
   const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : S;
-  const int kfull = a.ranges[((int64_t)b * a.nq + qb) * 2 + 0];
-  const int kend = a.ranges[((int64_t)b * a.nq + qb) * 2 + 1];
+  // with Gen Images the block walks its tile list (positions < kfull unmasked)
+  const bool hole = a.tiles != nullptr;
+  const int32_t* cnt = hole ? a.tile_count : a.ranges;
+  const int kfull = cnt[((int64_t)b * a.nq + qb) * 2 + 0];
+  const int kend = cnt[((int64_t)b * a.nq + qb) * 2 + 1];
+  const int32_t* tlist = hole ? a.tiles + ((int64_t)b * a.nq + qb) * a.nk : nullptr;
   const float cs = PRE ? 1.f : a.scale_log2e;
 
   f32x16 o[D / 32];
@@ -492,7 +530,8 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
   float qf[D / 2];
   for (int kk = 0; kk < D / 2; ++kk) qf[kk] = qp[2 * kk + hi];
 
-  for (int kb = 0; kb < kend; ++kb) {
+  for (int pos = 0; pos < kend; ++pos) {
+    const int kb = hole ? tlist[pos] : pos;
     __syncthreads();
     for (int e = tid; e < BK * D; e += C::NT) {
       const int key = e / D, d = e % D;
@@ -510,11 +549,11 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
       for (int kk = 0; kk < D / 2; ++kk)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * kk], qf[kk], s[kt], 0, 0, 0);
     }
-    if (kb >= kfull || (kb + 1) * BK > S) {
+    if (pos >= kfull || (kb + 1) * BK > S) {
       for (int kt = 0; kt < 2; ++kt)
         for (int r = 0; r < 16; ++r) {
           const int key = kb * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= lim) s[kt][r] = -INFINITY;
+          if (key >= lim || (hole && i >= a.key_vis[(int64_t)b * a.kv_stride + key])) s[kt][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -557,6 +596,21 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
 }
 
 // ====================================================================== launch
+template <int D, int G, bool HOLE>
+void launch_bf16(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(CfgB<D, G>::NT);
+  if (a.lse) {
+    if (a.q_prescaled)
+      hipLaunchKernelGGL((attn_bf16<D, G, true, true, HOLE>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_bf16<D, G, false, true, HOLE>), grid, block, 0, stream, a);
+  } else if (a.q_prescaled) {
+    hipLaunchKernelGGL((attn_bf16<D, G, true, false, HOLE>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_bf16<D, G, false, false, HOLE>), grid, block, 0, stream, a);
+  }
+}
+
 template <int D, int G>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.B * a.Hkv * a.nq_run;
@@ -568,17 +622,10 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((attn_f32<D, G, false>), grid, block, 0, stream, a);
   } else {
-    const dim3 block(CfgB<D, G>::NT);
-    if (a.lse) {
-      if (a.q_prescaled)
-        hipLaunchKernelGGL((attn_bf16<D, G, true, true>), grid, block, 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_bf16<D, G, false, true>), grid, block, 0, stream, a);
-    } else if (a.q_prescaled) {
-      hipLaunchKernelGGL((attn_bf16<D, G, true, false>), grid, block, 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((attn_bf16<D, G, false, false>), grid, block, 0, stream, a);
-    }
+    if (a.tiles)
+      launch_bf16<D, G, true>(a, grid, stream);
+    else
+      launch_bf16<D, G, false>(a, grid, stream);
   }
   return hipGetLastError();
 }

@@ -14,6 +14,15 @@
 // [kfull, kend) and SKIP beyond, where kfull comes from the block's smallest limit and
 // kend from its largest; the classifier writes those two integers, the per-row limits
 // and, on request, the explicit per-tile labels.
+//
+// Gen Images of a multi-image training sequence (HunyuanImage 3.0 digest, "Generalized
+// Causal Attention", the multi-generation training paragraph and Figure 4(b)) are hidden
+// from every token after them, which cuts holes into those prefixes. Pair (i, j) is then
+// allowed iff j < lim(i) and i < kvis(j), kvis(j) being the end of j's Gen Image (S for
+// other keys). A tile is FULL iff every row's limit covers it and every key's kvis lies
+// past the block's last row; it is SKIP when no row's limit reaches it or every key's kvis
+// is at or before the block's first row (exact for these segment kinds). For such layouts
+// the classifier also writes kvis and, per query block, the list of tiles to execute.
 #include "ha_internal.h"
 
 namespace ha {
@@ -62,10 +71,67 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyArgs a) {
     a.ranges[((int64_t)b * a.nq + qb) * 2 + 0] = kfull;
     a.ranges[((int64_t)b * a.nq + qb) * 2 + 1] = kend;
   }
+
+  // key visibility of keys [r0, r1) (the blocks cover [0, S) once), and of the padding
+  if (a.key_vis) {
+    int32_t* kv = a.key_vis + (int64_t)b * a.kv_stride;
+    for (int j = r0 + threadIdx.x; j < r1; j += kThreads) {
+      int vis = S;
+      for (int s = 0; s < a.seg.n_seg; ++s)
+        if (a.seg.kind[seg0 + s] == 3 && j >= a.seg.start[seg0 + s] && j < a.seg.end[seg0 + s])
+          vis = a.seg.end[seg0 + s];
+      kv[j] = vis;
+    }
+    if (qb == a.nq - 1)
+      for (int j = S + threadIdx.x; j < a.kv_stride; j += kThreads) kv[j] = 0;
+  }
+
+  // label of key tile kb: the range of kvis over its keys comes from the segment table
+  auto label = [&](int kb) {
+    const int c0 = kb * a.bk, c1 = min(c0 + a.bk, S);
+    if (!a.has_gen) return kb < kfull ? 1 : (kb < kend ? 2 : 0);
+    int vmin = S, vmax = 0;
+    for (int s = 0; s < a.seg.n_seg; ++s) {
+      const int st = a.seg.start[seg0 + s], en = a.seg.end[seg0 + s];
+      if (st >= c1 || en <= c0) continue;
+      const int vis = a.seg.kind[seg0 + s] == 3 ? en : S;
+      vmin = min(vmin, vis);
+      vmax = max(vmax, vis);
+    }
+    if (s_max <= c0 || vmax <= r0) return 0;
+    if (s_min >= c1 && vmin > r1 - 1) return 1;
+    return 2;
+  };
   if (a.labels) {
     uint8_t* row = a.labels + ((int64_t)b * a.nq + qb) * a.nk;
-    for (int kb = threadIdx.x; kb < a.nk; kb += kThreads)
-      row[kb] = kb < kfull ? 1 : (kb < kend ? 2 : 0);
+    for (int kb = threadIdx.x; kb < a.nk; kb += kThreads) row[kb] = (uint8_t)label(kb);
+  }
+
+  // the tiles to execute, in order: FULL tiles inside the sequence, then the others that
+  // are not SKIP (compacted by the first wave, 64 tiles per round)
+  if (a.tiles && threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int32_t* list = a.tiles + ((int64_t)b * a.nq + qb) * a.nk;
+    int n = 0, nfull = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int kb0 = 0; kb0 < a.nk; kb0 += 64) {
+        const int kb = kb0 + lane;
+        bool take = false;
+        if (kb < a.nk) {
+          const int lab = label(kb);
+          const bool inside_full = lab == 1 && (kb + 1) * a.bk <= S;
+          take = pass == 0 ? inside_full : (lab != 0 && !inside_full);
+        }
+        const unsigned long long m = __ballot(take);
+        if (take) list[n + __popcll(m & ((1ull << lane) - 1ull))] = kb;
+        n += __popcll(m);
+      }
+      if (pass == 0) nfull = n;
+    }
+    if (lane == 0) {
+      a.tile_count[((int64_t)b * a.nq + qb) * 2 + 0] = nfull;
+      a.tile_count[((int64_t)b * a.nq + qb) * 2 + 1] = n;
+    }
   }
 }
 

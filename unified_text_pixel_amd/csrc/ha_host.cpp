@@ -94,7 +94,7 @@ ha_status check_desc(const ha_attn_desc* d) {
     int64_t at = 0;
     for (int s = 0; s < d->n_segments; ++s) {
       const ha_segment& g = d->segments[(int64_t)b * d->n_segments + s];
-      if (g.kind != HA_SEG_CAUSAL && g.kind != HA_SEG_FULL && g.kind != HA_SEG_GCA)
+      if (g.kind != HA_SEG_CAUSAL && g.kind != HA_SEG_FULL && g.kind != HA_SEG_GCA && g.kind != HA_SEG_GEN)
         return fail(HA_ERR_SEGMENTS, "batch %d segment %d: unknown kind %d", b, s, g.kind);
       if (g.length <= 0)
         return fail(HA_ERR_SEGMENTS, "batch %d segment %d: length %d must be > 0", b, s, g.length);
@@ -111,6 +111,22 @@ ha_status check_desc(const ha_attn_desc* d) {
 }
 
 bool empty(const ha_attn_desc* d) { return d->batch == 0 || d->seq_len == 0; }
+
+// Some segment is a Gen Image (its keys are hidden from the tokens after it).
+bool has_gen(const ha_attn_desc* d) {
+  if (empty(d)) return false;
+  for (int64_t t = 0; t < (int64_t)d->batch * d->n_segments; ++t)
+    if (d->segments[t].kind == HA_SEG_GEN) return true;
+  return false;
+}
+
+// Plan arrays of a layout with Gen Images (null otherwise): key visibility and per query
+// block tile lists, written by the classifier and read by the attention kernels.
+struct HolePlan {
+  int32_t* key_vis = nullptr;
+  int32_t* tiles = nullptr;
+  int32_t* tile_count = nullptr;
+};
 
 ha_status check_tensor(const void* p, const char* name) {
   if (!p) return fail(HA_ERR_INVALID_ARG, "%s is NULL", name);
@@ -159,7 +175,7 @@ void tile_shape(const ha_attn_desc* d, int* bq, int* bk, int* nq, int* nk) {
 
 // Launch the classifier over batch chunks whose segment tables fit the kernel arguments.
 ha_status run_classify(const ha_attn_desc* d, uint8_t* labels, int32_t* ranges, int32_t* row_limit,
-                       hipStream_t stream) {
+                       hipStream_t stream, const HolePlan& hole = HolePlan{}) {
   ha::ClassifyArgs a{};
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
@@ -171,6 +187,11 @@ ha_status run_classify(const ha_attn_desc* d, uint8_t* labels, int32_t* ranges, 
   a.labels = labels;
   a.ranges = ranges;
   a.row_limit = row_limit;
+  a.has_gen = has_gen(d);
+  a.key_vis = hole.key_vis;
+  a.tiles = hole.tiles;
+  a.tile_count = hole.tile_count;
+  a.kv_stride = ha::key_vis_stride(d->seq_len);
   const int per_launch = ha::kArgSegs / d->n_segments;
   for (int b0 = 0; b0 < d->batch; b0 += per_launch) {
     const int n = std::min(per_launch, d->batch - b0);
@@ -244,7 +265,7 @@ ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const v
 
 ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const void* v, const int32_t* row_limit,
                    const int32_t* ranges, void* out, bool prescaled, hipStream_t stream, float* lse = nullptr,
-                   int row_begin = 0) {
+                   int row_begin = 0, const HolePlan& hole = HolePlan{}) {
   ha::AttnArgs a{};
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
@@ -268,12 +289,37 @@ ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const vo
   // ceil((S - row_begin) / bq) of them
   a.nq_run = (int)cdiv(d->seq_len - row_begin, bq);
   a.row_begin = row_begin;
+  a.key_vis = hole.key_vis;
+  a.tiles = hole.tiles;
+  a.tile_count = hole.tile_count;
+  a.kv_stride = ha::key_vis_stride(d->seq_len);
+  a.nk = nk;
   return check_launch(ha::launch_attn(a, stream), stream, "attention");
 }
 
 struct Workspace {
-  size_t row_limit, ranges, q_rot, k_rot, total;
+  size_t row_limit, ranges, q_rot, k_rot, key_vis, tiles, tile_count, total;
 };
+
+// Bytes of the Gen Image plan arrays, placed at *at (offsets into the workspace).
+void take_hole(const ha_attn_desc* d, int nq, int nk, size_t* at, size_t* key_vis, size_t* tiles,
+               size_t* tile_count) {
+  *key_vis = *at;
+  *at = round256(*at + (size_t)d->batch * ha::key_vis_stride(d->seq_len) * 4);
+  *tiles = *at;
+  *at = round256(*at + (size_t)d->batch * nq * nk * 4);
+  *tile_count = *at;
+  *at = round256(*at + (size_t)d->batch * nq * 2 * 4);
+}
+
+HolePlan hole_plan(const ha_attn_desc* d, char* ws, size_t key_vis, size_t tiles, size_t tile_count) {
+  HolePlan h;
+  if (!has_gen(d)) return h;
+  h.key_vis = reinterpret_cast<int32_t*>(ws + key_vis);
+  h.tiles = reinterpret_cast<int32_t*>(ws + tiles);
+  h.tile_count = reinterpret_cast<int32_t*>(ws + tile_count);
+  return h;
+}
 
 Workspace workspace_layout(const ha_attn_desc* d, bool prologue) {
   int bq, bk, nq, nk;
@@ -291,6 +337,7 @@ Workspace workspace_layout(const ha_attn_desc* d, bool prologue) {
     w.k_rot = at;
     at = round256(at + (size_t)d->batch * d->seq_len * d->n_kv_heads * d->head_dim * elem);
   }
+  if (has_gen(d)) take_hole(d, nq, nk, &at, &w.key_vis, &w.tiles, &w.tile_count);
   w.total = at;
   return w;
 }
@@ -306,7 +353,8 @@ ha_status check_train(const ha_attn_desc* d) {
 bool has_norm(const ha_prologue_desc* p) { return p && p->q_norm_weight; }
 
 struct BwdWorkspace {
-  size_t row_limit, ranges, q_rot, k_rot, delta, dq_rot, dk_rot, dwq, dwk, dw_scratch, total;
+  size_t row_limit, ranges, q_rot, k_rot, delta, dq_rot, dk_rot, dwq, dwk, dw_scratch, key_vis, tiles, tile_count,
+      total;
 };
 
 BwdWorkspace bwd_workspace_layout(const ha_attn_desc* d, bool norm) {
@@ -331,6 +379,7 @@ BwdWorkspace bwd_workspace_layout(const ha_attn_desc* d, bool norm) {
     take(w.dwk, B * S * D * 4);
     take(w.dw_scratch, (size_t)ha::dw_scratch_floats((int)D) * 4);
   }
+  if (has_gen(d)) take_hole(d, nq, nk, &at, &w.key_vis, &w.tiles, &w.tile_count);
   w.total = at;
   return w;
 }
@@ -429,6 +478,8 @@ ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const voi
   if (!row_limit || !ranges) return fail(HA_ERR_INVALID_ARG, "row_limit and ranges are required");
   if (!aligned(row_limit, 4) || !aligned(ranges, 4))
     return fail(HA_ERR_ALIGNMENT, "row_limit and ranges must be 4-byte aligned");
+  if (has_gen(desc))
+    return fail(HA_ERR_UNSUPPORTED, "Gen Image segments need the full tile plan: use ha_attn_fwd");
   st = run_attn(desc, q, k, v, row_limit, ranges, out, desc->q_prescaled == 1, static_cast<hipStream_t>(stream));
   return st == HA_OK ? ok() : st;
 }
@@ -452,7 +503,8 @@ ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const 
   int32_t* row_limit = reinterpret_cast<int32_t*>(ws + w.row_limit);
   int32_t* ranges = reinterpret_cast<int32_t*>(ws + w.ranges);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_classify(desc, nullptr, ranges, row_limit, s)) != HA_OK) return st;
+  const HolePlan hole = hole_plan(desc, ws, w.key_vis, w.tiles, w.tile_count);
+  if ((st = run_classify(desc, nullptr, ranges, row_limit, s, hole)) != HA_OK) return st;
   const void* qa = q;
   const void* ka = k;
   if (pro) {
@@ -462,7 +514,7 @@ ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const 
     qa = qr;
     ka = kr;
   }
-  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, pro != nullptr, s, lse);
+  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, pro != nullptr, s, lse, 0, hole);
   return st == HA_OK ? ok() : st;
 }
 
@@ -500,6 +552,8 @@ ha_status ha_attn_fwd_planned_from(const ha_attn_desc* desc, const void* q, cons
   if (!row_limit || !ranges) return fail(HA_ERR_INVALID_ARG, "row_limit and ranges are required");
   if (!aligned(row_limit, 4) || !aligned(ranges, 4))
     return fail(HA_ERR_ALIGNMENT, "row_limit and ranges must be 4-byte aligned");
+  if (has_gen(desc))
+    return fail(HA_ERR_UNSUPPORTED, "Gen Image segments need the full tile plan: use ha_attn_fwd");
   st = run_attn(desc, q, k, v, row_limit, ranges, out, desc->q_prescaled == 1, static_cast<hipStream_t>(stream),
                 nullptr, row_begin);
   return st == HA_OK ? ok() : st;
@@ -563,7 +617,8 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   float* dq_rot = reinterpret_cast<float*>(ws + w.dq_rot);
   float* dk_rot = reinterpret_cast<float*>(ws + w.dk_rot);
 
-  if ((st = run_classify(desc, nullptr, ranges, row_limit, s)) != HA_OK) return st;
+  const HolePlan hole = hole_plan(desc, ws, w.key_vis, w.tiles, w.tile_count);
+  if ((st = run_classify(desc, nullptr, ranges, row_limit, s, hole)) != HA_OK) return st;
   // q' = scale log2(e) (normalised, rotated q) and the rotated k, as the forward used them
   ha_prologue_desc plain{};
   plain.rope_kind = HA_ROPE_NONE;
@@ -592,6 +647,11 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   a.D = D;
   a.nq = nq;
   a.scale = (float)softmax_scale(desc);
+  a.key_vis = hole.key_vis;
+  a.tiles = hole.tiles;
+  a.tile_count = hole.tile_count;
+  a.kv_stride = ha::key_vis_stride(S);
+  a.nk = nk;
   if ((st = check_launch(ha::launch_bwd_dkdv(a, s), s, "backward dK dV")) != HA_OK) return st;
   if ((st = check_launch(ha::launch_bwd_dq(a, s), s, "backward dQ")) != HA_OK) return st;
   // through the rotary embedding and RMSNorm to the inputs

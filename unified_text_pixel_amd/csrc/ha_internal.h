@@ -19,11 +19,23 @@ struct SegArgs {
   int32_t kind[kArgSegs];
 };
 
+// Gen Images (multi-image training): key j is seen only by rows i < key_vis[j] (the end
+// of its Gen Image; S for every other key; 0 for the padding after S). Rows of key_vis
+// are key_vis_stride(S) long, a multiple of every key block the kernels read.
+constexpr int kKeyVisAlign = 256;
+inline int key_vis_stride(int S) { return (S + kKeyVisAlign - 1) / kKeyVisAlign * kKeyVisAlign; }
+
 struct ClassifyArgs {
   int32_t S, nq, nk, bq, bk;
   uint8_t* labels;     // [B][nq][nk] or null
-  int32_t* ranges;     // [B][nq][2] or null
-  int32_t* row_limit;  // [B][S] or null
+  int32_t* ranges;     // [B][nq][2] or null: key tiles by the row limits alone
+  int32_t* row_limit;  // [B][S] or null: the key prefix of each row before any hole
+  int32_t has_gen;     // some segment is a Gen Image (labels then account for the holes)
+  int32_t* key_vis;    // [B][key_vis_stride(S)] or null
+  int32_t* tiles;      // [B][nq][nk] or null: each query block's key tiles to execute,
+                       // FULL tiles inside the sequence first, then the rest
+  int32_t* tile_count; // [B][nq][2]: (inside FULL tiles, all listed tiles)
+  int32_t kv_stride;
   SegArgs seg;
 };
 hipError_t launch_classify(const ClassifyArgs& a, hipStream_t stream);
@@ -65,6 +77,11 @@ struct AttnArgs {
   float* lse;                // [B][Hq][S] row log-sum-exp (natural log), or null
   int32_t nq_run;            // compute the last nq_run query blocks of each (batch, KV head)
   int32_t row_begin;         // rows below it are computed with their block but not written
+  // Gen Image layouts (else null): the classifier's key visibility and tile lists
+  const int32_t* key_vis;
+  const int32_t* tiles;
+  const int32_t* tile_count;
+  int32_t kv_stride, nk;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
@@ -87,6 +104,11 @@ struct BwdArgs {
   void* dv;                  // bf16 [B][S][Hkv][D]
   int32_t B, S, Hq, Hkv, D, nq;
   float scale;               // softmax scale
+  // Gen Image layouts (else null), as in AttnArgs
+  const int32_t* key_vis;
+  const int32_t* tiles;
+  const int32_t* tile_count;
+  int32_t kv_stride, nk;
 };
 hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int B, int S, int Hq, int D,
                             hipStream_t stream);
