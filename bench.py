@@ -14,6 +14,10 @@ timed step, which gives the attention kernel's own duration for the MFMA rooflin
 the prologue's for its HBM roofline. Three copies of the inputs are cycled so the 256 MB
 Infinity Cache cannot serve a step from the previous one.
 
+"training_layouts" times ha_attn_fwd_lse and ha_attn_bwd whole on the multi-image
+training sequence (Gen Images hidden from the tokens after them) and on the same shape with
+plain image segments.
+
 "prefix_step" times a denoising step that reuses the causal text prefix (its rotated q, k
 and output rows) from an earlier step: the prologue and attention rows from the text end.
 
@@ -22,7 +26,7 @@ and reported under "backward" (8 d FLOP per allowed pair and query head); it is 
 of the step.
 
     python bench.py [--steps K] [--warmup W] [--workload hd2048] [--no-cpu-baseline] [--no-backward]
-                    [--no-prefix]
+                    [--no-prefix] [--no-training-layouts]
 """
 from __future__ import annotations
 
@@ -63,11 +67,15 @@ def attn_traffic():
 
 def allowed_pairs(segments: np.ndarray, S: int) -> int:
     """Allowed query-key pairs of one batch item, summed per segment in closed form:
-    causal [a, a+L) -> sum (i+1); full -> L*S; image (generalized causal) -> L*(a+L)."""
+    causal [a, a+L) -> sum (i+1); full -> L*S; image (generalized causal or Gen Image) ->
+    L*(a+L); then each Gen Image's L keys are removed from the S - (a+L) rows after it."""
     n = 0
     for a, L, kind in segments:
         a, L = int(a), int(L)
         n += L * a + L * (L + 1) // 2 if kind == 0 else (L * S if kind == 1 else L * (a + L))
+    for a, L, kind in segments:
+        if kind == 3:
+            n -= int(L) * (S - int(a) - int(L))
     return n
 
 
@@ -148,6 +156,64 @@ def prefix_leg(w, x, sets, desc, pro, stream, step, warmup, steps):
             "attn_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
 
 
+def training_layout_leg(names, warmup, steps):
+    """Training forward (ha_attn_fwd_lse) and backward (ha_attn_bwd) of whole layouts,
+    each call timed alone with HIP events on the launch stream: the multi-image training
+    sequence (Gen Images hidden from later tokens) beside the same shape with plain image
+    segments. Useful FLOPs: 4 d per allowed pair and query head forward, 8 d backward."""
+    import torch
+    import workloads as W
+    from unified_text_pixel_amd import api, binding as B
+    from workloads.device import to_device
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name in names:
+        w = W.get_config(name)
+        x = W.generate(w)
+        dev = to_device(x)
+        desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments)
+        cs = api.rope_table(w.rope_theta, w.head_dim, w.seq_len) if w.rope != "none" else None
+        pro = B.PrologueDesc(w.rope, dev["positions"], cs, 0 if cs is None else cs.shape[0],
+                             dev["w_q"], dev["w_k"], w.norm_eps, w.mrope_sections)
+        ws = torch.empty(max(B.ha_attn_workspace_bytes(desc, pro), B.ha_attn_bwd_workspace_bytes(desc, pro)),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(dev["q"])
+        lse = torch.empty((w.batch, w.n_q_heads, w.seq_len), dtype=torch.float32, device="cuda")
+        dout = torch.randn(dev["q"].shape, generator=torch.Generator(device="cuda").manual_seed(7),
+                           device="cuda").to(torch.bfloat16)
+        dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
+        dw = [torch.empty(w.head_dim, device="cuda") if w.qk_norm else None for _ in range(2)]
+
+        def fwd():
+            B.ha_attn_fwd_lse(desc, pro, dev["q"], dev["k"], dev["v"], out, lse, ws, stream=stream)
+
+        def bwd():
+            B.ha_attn_bwd(desc, pro, dev["q"], dev["k"], dev["v"], out, lse, dout, dq, dk, dv, dw[0], dw[1], ws,
+                          stream=stream)
+
+        def timed(fn, n):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+            torch.cuda.synchronize()
+            for e in ev:
+                e[0].record(stream)
+                fn()
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+
+        for _ in range(max(1, warmup // 2)):
+            fwd()
+            bwd()
+        n = max(5, steps // 4)
+        fms, bms = timed(fwd, n), timed(bwd, n)
+        pairs = sum(allowed_pairs(x.segments[b], w.seq_len) for b in range(w.batch))
+        flop = 4.0 * w.head_dim * w.n_q_heads * pairs
+        res[name] = {"segments": x.segments[0].tolist(), "allowed_pairs": pairs,
+                     "fwd_lse_ms": fms, "fwd_tflops": flop / (fms / 1e3) / 1e12,
+                     "bwd_ms": bms, "bwd_tflops": 2 * flop / (bms / 1e3) / 1e12, "calls": n}
+    return res
+
+
 def backward_leg(w, x, dev, useful_fwd, stream, warmup, steps, nsets):
     """Training backward (ha_attn_bwd: rebuilt prologue, dK/dV, dQ, rotary and RMSNorm
     backward) after a forward with lse, timed alone with HIP events on the launch stream.
@@ -208,6 +274,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-prefix", action="store_true")
+    ap.add_argument("--no-training-layouts", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -325,6 +392,8 @@ def main():
         rec["prefix_step"] = prefix_leg(w, x, sets, desc, pro, stream, step, args.warmup, args.steps)
     if not args.no_backward and w.dtype == "bf16":
         rec["backward"] = backward_leg(w, x, dev, useful, stream, args.warmup, args.steps, args.sets)
+    if not args.no_training_layouts:
+        rec["training_layouts"] = training_layout_leg(["hunyuan_multigen", "hunyuan"], args.warmup, args.steps)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, x)
