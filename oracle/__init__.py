@@ -15,6 +15,8 @@ What it computes, slowly and plainly, in float64 unless a function says otherwis
   pipeline.py   the whole path in the pages' order: norm, rotary, mask, attention
   brute.py      scalar pure-Python fp64 re-derivation for tiny inputs
   backward.py   gradients of the whole path (attention, rotary, norm) and the row lse
+  projection.py the QKV projection feeding the prologue (x W^T, split by heads, then norm
+                and rotary)
 
 Parity pins (tests/test_oracle_*.py) tie each part to something other than itself:
 closed-form allowed-pair counts, library routines (torch CPU scaled_dot_product_attention
@@ -32,6 +34,7 @@ from .tiles import tile_labels
 from .pipeline import prologue, hot_path, hot_path_rows
 from .backward import (attention_lse, attention_backward, rope_backward, rms_norm_backward,
                        path_lse, path_backward)
+from .projection import qkv_projection, qkv_prologue
 
 SEG_CAUSAL, SEG_FULL, SEG_GCA, SEG_GEN = 0, 1, 2, 3
 LABEL_SKIP, LABEL_FULL, LABEL_PARTIAL = 0, 1, 2

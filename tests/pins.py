@@ -385,6 +385,53 @@ def pin_tile_labels():
             assert np.array_equal(oracle.tile_labels(M, bq, bk, q_end_aligned=True),
                                   closed_form_labels(t, S, bq, bk, q_end_aligned=True)), (t.tolist(), bq)
 
+# ---------------------------------------------------------------- QKV projection (oracle/projection.py)
+def pin_projection_permutation():
+    """A permutation weight picks input channels: y[..., i] = x[..., perm[i]] exactly, so
+    q, k, v are known slices of x. Catches a transposed weight (which applies the inverse
+    permutation) and a wrong order of the q, k and v sections."""
+    w = small_workload([W.Segment(C, 6)], hq=4, hkv=2, d=8, rope="none", norm=False, batch=2)
+    n_out = (w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(n_out)
+    P = np.zeros((n_out, n_out))
+    P[np.arange(n_out), perm] = 1.0
+    x = rng.standard_normal((w.batch, w.seq_len, n_out))
+    q, k, v = oracle.qkv_projection(x, P, w.n_q_heads, w.n_kv_heads, w.head_dim)
+    y = x[..., perm]
+    nq, nkv = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    assert np.array_equal(q, y[..., :nq].reshape(q.shape))
+    assert np.array_equal(k, y[..., nq:nq + nkv].reshape(k.shape))
+    assert np.array_equal(v, y[..., nq + nkv:].reshape(v.shape))
+
+
+def pin_projection_bruteforce():
+    """Scalar loops for the product, then the scalar norm and rotary of oracle/brute.py, per
+    head: equal to the vectorised projection + prologue to rounding."""
+    from oracle.brute import _axis_list, _prep
+    for rope, sections in (("mrope", (2, 1, 1)), ("2d", (0, 0, 0))):
+        w = small_workload([W.Segment(C, 3), W.Segment(F, 4, (2, 2))], hq=2, hkv=1, d=8, rope=rope,
+                           sections=sections, norm=True, seed=9)
+        x_in = W.generate(w)
+        proj = W.generate_projection(w, hidden=12)
+        q_rot, k_rot, v = oracle.qkv_prologue(x_in, proj.x, proj.w_qkv)
+        axes = _axis_list(w.rope, w.head_dim // 2, w.mrope_sections)
+        d = w.head_dim
+        for t in range(w.seq_len):
+            y = [sum(float(proj.x[0, t, c]) * float(proj.w_qkv[n, c]) for c in range(12))
+                 for n in range(proj.w_qkv.shape[0])]
+            pos = x_in.positions[0, t]
+            for h in range(w.n_q_heads):
+                want = _prep(y[h * d:(h + 1) * d], w, x_in.w_q, pos, axes)
+                assert np.allclose(q_rot[0, t, h], want, rtol=1e-12, atol=1e-12), (rope, t, h)
+            base = w.n_q_heads * d
+            for g in range(w.n_kv_heads):
+                want = _prep(y[base + g * d:base + (g + 1) * d], w, x_in.w_k, pos, axes)
+                assert np.allclose(k_rot[0, t, g], want, rtol=1e-12, atol=1e-12), (rope, t, g)
+                vb = base + w.n_kv_heads * d
+                assert np.allclose(v[0, t, g], y[vb + g * d:vb + (g + 1) * d], rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- backward (oracle/backward.py)
 
 def _bwd_layout(rope="mrope", norm=True, batch=1, seed=21):

@@ -10,6 +10,7 @@ import oracle.mask
 import oracle.masked_attention
 import oracle.norm
 import oracle.pipeline
+import oracle.projection
 import oracle.rope
 import pins
 
@@ -99,6 +100,20 @@ def _mask_gen_variant(strict=False, none=False, own_rows=False):
     return mask_rows
 
 
+def _proj_variant(transposed=False, kv_swapped=False):
+    def qkv_projection(x, w_qkv, n_q_heads, n_kv_heads, head_dim, dtype=np.float64):
+        x = np.asarray(x, dtype=dtype)
+        w = np.asarray(w_qkv, dtype=dtype)
+        B, S, _ = x.shape
+        y = x @ w if transposed else x @ w.T
+        nq, nkv = n_q_heads * head_dim, n_kv_heads * head_dim
+        q = y[..., :nq].reshape(B, S, n_q_heads, head_dim)
+        k = y[..., nq:nq + nkv].reshape(B, S, n_kv_heads, head_dim)
+        v = y[..., nq + nkv:nq + 2 * nkv].reshape(B, S, n_kv_heads, head_dim)
+        return (q, v, k) if kv_swapped else (q, k, v)
+    return qkv_projection
+
+
 _orig_mask_rows = oracle.mask.mask_rows
 _orig_attention = oracle.masked_attention.attention
 
@@ -167,6 +182,12 @@ MUTATIONS = {
                          ["pin_pair_counts", "pin_mask_gen_hole", "pin_mask_elementwise_bruteforce"]),
     "mask_gen_hidden_from_itself": ([(oracle.mask, "mask_rows", _mask_gen_variant(own_rows=True))],
                                     ["pin_pair_counts", "pin_mask_gen_hole", "pin_mask_elementwise_bruteforce"]),
+    "projection_transposed_weight": ([(oracle.projection, "qkv_projection", _proj_variant(transposed=True)),
+                                      (oracle, "qkv_projection", _proj_variant(transposed=True))],
+                                     ["pin_projection_permutation", "pin_projection_bruteforce"]),
+    "projection_k_v_swapped": ([(oracle.projection, "qkv_projection", _proj_variant(kv_swapped=True)),
+                                (oracle, "qkv_projection", _proj_variant(kv_swapped=True))],
+                               ["pin_projection_permutation", "pin_projection_bruteforce"]),
     "attn_dropped_scale": ([(oracle.masked_attention, "attention", _attn_no_scale)],
                            ["pin_attention_library"]),
     "attn_k_used_as_v": ([(oracle.masked_attention, "attention", _attn_k_for_v)],

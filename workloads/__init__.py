@@ -9,8 +9,9 @@ no normalisation, no rotary embedding, no attention).
 from .configs import (SEG_CAUSAL, SEG_FULL, SEG_GCA, SEG_GEN, Segment, Workload, CONFIGS,
                       get_config, page_shape_configs)
 from .generate import (Inputs, generate, positions_for, segment_table, f32_to_bf16_bits,
-                       bf16_bits_to_f32)
+                       bf16_bits_to_f32, ProjectionInputs, generate_projection)
 
 __all__ = ["SEG_CAUSAL", "SEG_FULL", "SEG_GCA", "SEG_GEN", "Segment", "Workload", "CONFIGS",
            "get_config", "page_shape_configs", "Inputs", "generate", "positions_for",
-           "segment_table", "f32_to_bf16_bits", "bf16_bits_to_f32"]
+           "segment_table", "f32_to_bf16_bits", "bf16_bits_to_f32", "ProjectionInputs",
+           "generate_projection"]

@@ -25,3 +25,8 @@ def to_device(inputs, device="cuda"):
         "w_k": None if inputs.w_k is None else torch.from_numpy(inputs.w_k).to(device),
     }
     return d
+
+
+def projection_to_device(p, device="cuda"):
+    """(x, w_qkv) as bf16 device tensors."""
+    return _t(p.x_bits, True, device), _t(p.w_bits, True, device)

@@ -112,3 +112,25 @@ def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
         w_k = (1.0 + 0.02 * rng.standard_normal(size=(d,), dtype=np.float32)).astype(np.float32)
     return Inputs(workload=w, q=q, k=k, v=v, q_bits=qb, k_bits=kb, v_bits=vb, w_q=w_q, w_k=w_k,
                   positions=positions_for(w), segments=segment_table(w))
+
+
+@dataclass
+class ProjectionInputs:
+    """Inputs of the QKV projection in front of the path: the layer's hidden states and the
+    fused q/k/v weight, both bf16 values (float32 arrays holding them, plus the patterns)."""
+    x: np.ndarray        # float32 [B][S][hidden]
+    x_bits: np.ndarray   # uint16
+    w_qkv: np.ndarray    # float32 [(Hq + 2 Hkv) d][hidden]
+    w_bits: np.ndarray   # uint16
+
+
+def generate_projection(w: Workload, hidden: int, seed: Optional[int] = None) -> ProjectionInputs:
+    """x ~ N(0, 1) and W ~ N(0, 1/hidden) (so each projected value is about N(0, 1)), drawn
+    in that order from their own stream and rounded to bf16."""
+    rng = np.random.Generator(np.random.PCG64(1000 + (w.seed if seed is None else seed)))
+    n_out = (w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim
+    x, xb = _draw(rng, (w.batch, w.seq_len, hidden), True)
+    wd = rng.standard_normal(size=(n_out, hidden), dtype=np.float32) * np.float32(1.0 / np.sqrt(hidden))
+    wb = f32_to_bf16_bits(wd)
+    return ProjectionInputs(x=x, x_bits=xb, w_qkv=bf16_bits_to_f32(wb).reshape(wd.shape),
+                            w_bits=wb.reshape(wd.shape))
