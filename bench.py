@@ -14,6 +14,10 @@ timed step, which gives the attention kernel's own duration for the MFMA rooflin
 the prologue's for its HBM roofline. Three copies of the inputs are cycled so the 256 MB
 Infinity Cache cannot serve a step from the previous one.
 
+"qkv_projection" times the step before the path, the layer's QKV projection with the
+prologue in its epilogue (ha_qkv_prologue), against three hipBLASLt projections plus
+ha_qk_prologue.
+
 "training_layouts" times ha_attn_fwd_lse and ha_attn_bwd whole on the multi-image
 training sequence (Gen Images hidden from the tokens after them) and on the same shape with
 plain image segments.
@@ -26,7 +30,7 @@ and reported under "backward" (8 d FLOP per allowed pair and query head); it is 
 of the step.
 
     python bench.py [--steps K] [--warmup W] [--workload hd2048] [--no-cpu-baseline] [--no-backward]
-                    [--no-prefix] [--no-training-layouts]
+                    [--no-prefix] [--no-training-layouts] [--no-qkv]
 """
 from __future__ import annotations
 
@@ -156,6 +160,65 @@ def prefix_leg(w, x, sets, desc, pro, stream, step, warmup, steps):
             "attn_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
 
 
+def qkv_leg(w, x, dev, stream, warmup, steps, hidden=4096):
+    """The step before the path: the layer's QKV projection (hidden 4096 -> (Hq + 2 Hkv) d)
+    with the prologue in its epilogue (ha_qkv_prologue), against the unfused route: three
+    torch linear calls (hipBLASLt) into contiguous q, k, v, then ha_qk_prologue. Each call
+    timed alone with HIP events on the launch stream, median of max(5, K/4) calls."""
+    import torch
+    import torch.nn.functional as Fn
+    import workloads as W
+    from unified_text_pixel_amd import api, binding as B
+    from workloads.device import projection_to_device
+    proj = W.generate_projection(w, hidden)
+    xd, wd = projection_to_device(proj)
+    desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments)
+    cs = api.rope_table(w.rope_theta, w.head_dim, w.seq_len) if w.rope != "none" else None
+    pro = B.PrologueDesc(w.rope, dev["positions"], cs, 0 if cs is None else cs.shape[0], dev["w_q"], dev["w_k"],
+                         w.norm_eps, w.mrope_sections, q_out_scale=B.ha_q_prescale(desc))
+    T, nq, nkv = w.batch * w.seq_len, w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    q = torch.empty((w.batch, w.seq_len, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((w.batch, w.seq_len, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    x2 = xd.view(T, hidden)
+    wq, wk, wv = wd[:nq], wd[nq:nq + nkv], wd[nq + nkv:]
+
+    def fused():
+        B.ha_qkv_prologue(desc, pro, xd, hidden, wd, q, k, v, stream=stream)
+
+    def gemms():
+        torch.matmul(x2, wq.t(), out=q.view(T, nq))
+        torch.matmul(x2, wk.t(), out=k.view(T, nkv))
+        torch.matmul(x2, wv.t(), out=v.view(T, nkv))
+
+    def prologue():
+        B.ha_qk_prologue(desc, pro, q, k, qr, kr, stream=stream)
+
+    def timed(fn):
+        for _ in range(max(1, warmup // 2)):
+            fn()
+        n = max(5, steps // 4)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in ev])), n
+
+    fms, n = timed(fused)
+    gms, _ = timed(gemms)
+    pms, _ = timed(prologue)
+    flop = 2.0 * T * hidden * (nq + 2 * nkv)
+    tf = flop / (fms / 1e3) / 1e12
+    return {"tokens": T, "hidden": hidden, "outputs": nq + 2 * nkv, "gflop": flop / 1e9,
+            "fused_ms": fms, "fused_tflops": tf, "fused_frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+            "unfused_gemm_ms": gms, "unfused_gemm_tflops": flop / (gms / 1e3) / 1e12,
+            "unfused_prologue_ms": pms, "unfused_total_ms": gms + pms, "calls": n}
+
+
 def training_layout_leg(names, warmup, steps):
     """Training forward (ha_attn_fwd_lse) and backward (ha_attn_bwd) of whole layouts,
     each call timed alone with HIP events on the launch stream: the multi-image training
@@ -275,6 +338,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-prefix", action="store_true")
     ap.add_argument("--no-training-layouts", action="store_true")
+    ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -392,6 +456,8 @@ def main():
         rec["prefix_step"] = prefix_leg(w, x, sets, desc, pro, stream, step, args.warmup, args.steps)
     if not args.no_backward and w.dtype == "bf16":
         rec["backward"] = backward_leg(w, x, dev, useful, stream, args.warmup, args.steps, args.sets)
+    if not args.no_qkv and w.head_dim == 128 and w.dtype == "bf16":
+        rec["qkv_projection"] = qkv_leg(w, x, dev, stream, args.warmup, args.steps)
     if not args.no_training_layouts:
         rec["training_layouts"] = training_layout_leg(["hunyuan_multigen", "hunyuan"], args.warmup, args.steps)
     if not args.no_cpu_baseline:

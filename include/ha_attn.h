@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 3
+#define HA_ABI_VERSION 4
 #define HA_MAX_SEGMENTS 64      /* segments per batch item */
 #define HA_MAX_SEQ_LEN (1 << 22)
 
@@ -207,6 +207,24 @@ ha_status ha_qk_prologue_from(const ha_attn_desc* desc, const ha_prologue_desc* 
 ha_status ha_attn_fwd_planned_from(const ha_attn_desc* desc, const void* q, const void* k,
                                    const void* v, const int32_t* row_limit, const int32_t* ranges,
                                    void* out, int32_t row_begin, void* stream);
+
+/* ---------------------------------------------------------------- QKV projection
+ * The step before the path: each backbone layer projects its normalised hidden states to
+ * q, k and v by one linear map (hidream-o1-p100a model card, "What this model is": hidden
+ * 4096, GQA 32/8, head dim 128, q/k RMSNorm, mRoPE). This call computes the projection on
+ * the matrix cores and applies the prologue (see ha_qk_prologue) to q and k in the same
+ * kernel, before anything is written, so q, k and v reach HBM once, in bf16, in the
+ * layouts ha_attn_fwd_planned reads:
+ *   x      DEVICE bf16 [batch][seq_len][hidden], hidden a positive multiple of 64
+ *   w_qkv  DEVICE bf16 [(n_q_heads + 2 n_kv_heads) * 128][hidden]: the linear layer's
+ *          weight, rows the q heads, then the k heads, then the v heads; y = x w_qkv^T,
+ *          no bias, accumulated in fp32 and not rounded before the prologue
+ *   q_out  [batch][seq_len][n_q_heads][128], k_out and v_out [batch][seq_len][n_kv_heads][128]
+ * pro may be NULL (a plain projection); its q_out_scale multiplies q (0 means 1). bf16 and
+ * head_dim 128 only (else HA_ERR_UNSUPPORTED). The segment table is not consulted. */
+ha_status ha_qkv_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* x,
+                          int32_t hidden, const void* w_qkv, void* q_out, void* k_out, void* v_out,
+                          void* stream);
 
 /* ---------------------------------------------------------------- training
  * The pages train these models end to end (HiDream-O1 atlas page, "How it works";

@@ -25,10 +25,10 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = U.load_library()
     names = declared_functions()
-    assert len(names) == 15 and sorted(B.EXPORTS) == names
+    assert len(names) == 16 and sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
-    assert U.ha_abi_version() == 3
+    assert U.ha_abi_version() == 4
 
 
 def seg(rows, batch=1):

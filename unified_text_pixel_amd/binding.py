@@ -28,7 +28,7 @@ ROPE_KINDS = {"none": HA_ROPE_NONE, "1d": HA_ROPE_1D, "2d": HA_ROPE_2D, "mrope":
 EXPORTS = ("ha_abi_version", "ha_last_error", "ha_rope_table_fill", "ha_q_prescale",
            "ha_tile_shape", "ha_classify_tiles", "ha_qk_prologue", "ha_attn_workspace_bytes",
            "ha_attn_fwd_planned", "ha_attn_fwd", "ha_attn_fwd_lse", "ha_attn_bwd_workspace_bytes",
-           "ha_attn_bwd", "ha_qk_prologue_from", "ha_attn_fwd_planned_from")
+           "ha_attn_bwd", "ha_qk_prologue_from", "ha_attn_fwd_planned_from", "ha_qkv_prologue")
 
 
 class HAError(RuntimeError):
@@ -88,6 +88,7 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
         "ha_attn_bwd": ([D, PD, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "ha_qk_prologue_from": ([D, PD, P, P, P, P, I32, P], ctypes.c_int),
         "ha_attn_fwd_planned_from": ([D, P, P, P, P, P, P, I32, P], ctypes.c_int),
+        "ha_qkv_prologue": ([D, PD, P, I32, P, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -250,3 +251,8 @@ def ha_qk_prologue_from(desc: AttnDesc, pro: PrologueDesc, q_in, k_in, q_out, k_
 def ha_attn_fwd_planned_from(desc: AttnDesc, q, k, v, row_limit, ranges, out, row_begin: int, stream=None):
     _check(load_library().ha_attn_fwd_planned_from(_d(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(row_limit),
                                                    _ptr(ranges), _ptr(out), int(row_begin), _stream(stream)))
+
+
+def ha_qkv_prologue(desc: AttnDesc, pro, x, hidden: int, w_qkv, q_out, k_out, v_out, stream=None):
+    _check(load_library().ha_qkv_prologue(_d(desc), _pd(pro), _ptr(x), int(hidden), _ptr(w_qkv), _ptr(q_out),
+                                          _ptr(k_out), _ptr(v_out), _stream(stream)))

@@ -574,6 +574,49 @@ ha_status ha_attn_fwd_lse(const ha_attn_desc* desc, const ha_prologue_desc* pro,
   return attn_fwd(desc, pro, q, k, v, out, lse, workspace, workspace_bytes, stream);
 }
 
+ha_status ha_qkv_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* x, int32_t hidden,
+                          const void* w_qkv, void* q_out, void* k_out, void* v_out, void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if (pro && (st = check_prologue(desc, pro)) != HA_OK) return st;
+  if (desc->dtype != HA_DTYPE_BF16) return fail(HA_ERR_UNSUPPORTED, "ha_qkv_prologue takes bf16 tensors");
+  if (desc->head_dim != 128) return fail(HA_ERR_UNSUPPORTED, "ha_qkv_prologue: head_dim %d; supported: 128", desc->head_dim);
+  if (hidden < 64 || hidden % 64 != 0)
+    return fail(HA_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 64", hidden);
+  if (empty(desc)) return ok();
+  const void* tensors[] = {x, w_qkv, q_out, k_out, v_out};
+  const char* names[] = {"x", "w_qkv", "q_out", "k_out", "v_out"};
+  for (int t = 0; t < 5; ++t)
+    if ((st = check_tensor(tensors[t], names[t])) != HA_OK) return st;
+  ha::QkvArgs a{};
+  a.x = x;
+  a.w = w_qkv;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.T = desc->batch * desc->seq_len;
+  a.K = hidden;
+  a.Hq = desc->n_q_heads;
+  a.Hkv = desc->n_kv_heads;
+  a.q_scale = pro && pro->q_out_scale > 0.f ? pro->q_out_scale : 1.f;
+  a.rotate = pro && pro->rope_kind != HA_ROPE_NONE;
+  if (a.rotate) {
+    a.positions = pro->positions;
+    a.cos_sin = pro->cos_sin;
+    a.n_pos = pro->n_pos;
+    a.n_axes = n_axes_of(pro->rope_kind);
+    axis_table(pro, desc->head_dim, a.axis);
+  }
+  if (has_norm(pro)) {
+    a.wq = pro->q_norm_weight;
+    a.wk = pro->k_norm_weight;
+    a.eps = pro->eps;
+  }
+  st = check_launch(ha::launch_qkv(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
+                    "qkv projection");
+  return st == HA_OK ? ok() : st;
+}
+
 size_t ha_attn_bwd_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro) {
   if (check_desc(desc) != HA_OK) return 0;
   return bwd_workspace_layout(desc, has_norm(pro)).total;

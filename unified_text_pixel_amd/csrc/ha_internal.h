@@ -85,6 +85,24 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
+// ---- QKV projection with the prologue in its epilogue (ha_qkv.hip)
+struct QkvArgs {
+  const void* x;             // bf16 [T][K]
+  const void* w;             // bf16 [(Hq + 2 Hkv) 128][K], rows q heads, k heads, v heads
+  void* q_out;               // bf16 [T][Hq][128]
+  void* k_out;               // bf16 [T][Hkv][128]
+  void* v_out;               // bf16 [T][Hkv][128]
+  const int32_t* positions;  // [T][n_axes] (rotate)
+  const float* cos_sin;      // [n_pos][64][2]
+  const float* wq;           // [128] or null (no RMSNorm)
+  const float* wk;
+  int32_t T, K, Hq, Hkv, n_axes, n_pos, rotate;
+  float eps, q_scale;
+  uint8_t axis[64];
+};
+int qkv_block_tokens();
+hipError_t launch_qkv(const QkvArgs& a, hipStream_t stream);
+
 // ---- backward (ha_attn_bwd.hip, ha_prologue.hip)
 
 // Key block of the dK/dV kernel: 32 keys per wave, 8 / G waves per query head.
