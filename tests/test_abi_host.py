@@ -76,6 +76,7 @@ def test_bad_descriptor_rejected_everywhere(kw, status, text):
         lambda: U.ha_qk_prologue_from(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, 0, stream=0),
         lambda: U.ha_attn_bwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                               FAKE, 1 << 30, stream=0),
+        lambda: U.ha_qkv_prologue(d, None, FAKE, 256, FAKE, FAKE, FAKE, FAKE, stream=0),
     ]
     for call in calls:
         with pytest.raises(U.HAError) as e:
@@ -275,3 +276,31 @@ def test_gen_image_layouts():
     assert U.ha_attn_workspace_bytes(d) - U.ha_attn_workspace_bytes(plain) >= extra
     bd, bp = bf16_desc(segments=g), bf16_desc(segments=seg([[0, 16, 0], [16, 32, 2], [48, 32, 0]]))
     assert U.ha_attn_bwd_workspace_bytes(bd) - U.ha_attn_bwd_workspace_bytes(bp) >= extra
+
+
+def test_qkv_projection_rejects_before_launch():
+    bf = bf16_desc()
+    cases = [
+        (lambda: U.ha_qkv_prologue(desc(), None, FAKE, 256, FAKE, FAKE, FAKE, FAKE, stream=0),
+         B.HA_ERR_UNSUPPORTED, "bf16"),
+        (lambda: U.ha_qkv_prologue(bf16_desc(head_dim=64), None, FAKE, 256, FAKE, FAKE, FAKE, FAKE, stream=0),
+         B.HA_ERR_UNSUPPORTED, "head_dim"),
+        (lambda: U.ha_qkv_prologue(bf, None, FAKE, 100, FAKE, FAKE, FAKE, FAKE, stream=0),
+         B.HA_ERR_UNSUPPORTED, "multiple of 64"),
+        (lambda: U.ha_qkv_prologue(bf, None, FAKE, 0, FAKE, FAKE, FAKE, FAKE, stream=0),
+         B.HA_ERR_UNSUPPORTED, "multiple of 64"),
+        (lambda: U.ha_qkv_prologue(bf, None, None, 256, FAKE, FAKE, FAKE, FAKE, stream=0),
+         B.HA_ERR_INVALID_ARG, "x is NULL"),
+        (lambda: U.ha_qkv_prologue(bf, None, FAKE, 256, FAKE + 8, FAKE, FAKE, FAKE, stream=0),
+         B.HA_ERR_ALIGNMENT, "w_qkv"),
+        (lambda: U.ha_qkv_prologue(bf, U.PrologueDesc("2d"), FAKE, 256, FAKE, FAKE, FAKE, FAKE, stream=0),
+         B.HA_ERR_INVALID_ARG, "required"),
+    ]
+    for call, status, text in cases:
+        with pytest.raises(U.HAError) as e:
+            call()
+        assert e.value.status == status and text in str(e.value), str(e.value)
+    # no tokens: nothing to do, no launch
+    U.ha_qkv_prologue(bf16_desc(batch=0, segments=np.zeros((0, 0, 3))), None, None, 256, None, None, None, None,
+                      stream=0)
+    assert U.ha_last_error() == ""
