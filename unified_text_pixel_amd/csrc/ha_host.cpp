@@ -612,7 +612,13 @@ ha_status ha_qkv_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
     a.wk = pro->k_norm_weight;
     a.eps = pro->eps;
   }
-  st = check_launch(ha::launch_qkv(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
+  int dev = 0, n_cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    n_cus = 0;  // unknown: every token goes to the half-height tiles
+    (void)hipGetLastError();  // not reported by the launch check below
+  }
+  st = check_launch(ha::launch_qkv(a, n_cus, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
                     "qkv projection");
   return st == HA_OK ? ok() : st;
 }

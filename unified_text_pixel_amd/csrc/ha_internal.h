@@ -97,11 +97,12 @@ struct QkvArgs {
   const float* wq;           // [128] or null (no RMSNorm)
   const float* wk;
   int32_t T, K, Hq, Hkv, n_axes, n_pos, rotate;
+  int32_t m_begin;           // first token of this launch (tokens [m_begin, T))
   float eps, q_scale;
   uint8_t axis[64];
 };
 int qkv_block_tokens();
-hipError_t launch_qkv(const QkvArgs& a, hipStream_t stream);
+hipError_t launch_qkv(const QkvArgs& a, int n_cus, hipStream_t stream);
 
 // ---- backward (ha_attn_bwd.hip, ha_prologue.hip)
 

@@ -129,7 +129,7 @@ __global__ __launch_bounds__((CfgP<WN, WM, MT, BK, NST>::NT), 1) void qkv_kernel
   __shared__ __attribute__((aligned(1024))) char w3[NST > 3 ? C::WBYTES : 1024];
   __shared__ __attribute__((aligned(1024))) char w4[NST > 4 ? C::WBYTES : 1024];
 
-  const int nM = (a.T + C::BM - 1) / C::BM;
+  const int nM = (a.T - a.m_begin + C::BM - 1) / C::BM;
   const int n_heads = a.Hq + 2 * a.Hkv;
   const int nN = (n_heads + WN - 1) / WN;
   int mtile, ntile;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__((CfgP<WN, WM, MT, BK, NST>::NT), 1) void qkv_kernel
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WN, wm = wave / WN;
   const int hi = lane >> 5, ln = lane & 31;
-  const int m0 = mtile * C::BM;                 // first token of the workgroup
+  const int m0 = a.m_begin + mtile * C::BM;     // first token of the workgroup
   const int f0 = ntile * C::BN;                 // first feature of the workgroup
   const int nfeat = n_heads * HD;
   const __bf16* xg = static_cast<const __bf16*>(a.x);
@@ -305,22 +305,48 @@ __global__ __launch_bounds__((CfgP<WN, WM, MT, BK, NST>::NT), 1) void qkv_kernel
   }
 }
 
-// The kernel's configuration: 2 heads x 256 tokens per workgroup, 8 waves, K in stages of
-// 32 in a ring of 5 (160 KB of LDS: three stages in flight behind the one computed).
-constexpr int kWN = 2, kWM = 4, kMT = 2, kBK = 32, kNST = 5;
+// The kernel's configurations: 2 heads x 256 tokens per workgroup (8 waves of 128 features x
+// 64 tokens), and for the tail 2 heads x 128 tokens (8 waves of 128 x 32); K in stages of 32
+// in a ring of 5 (160 KB of LDS: three stages in flight behind the one computed).
+constexpr int kWN = 2, kWM = 4, kBK = 32, kNST = 5;
+using Main = CfgP<kWN, kWM, 2, kBK, kNST>;
+using Tail = CfgP<kWN, kWM, 1, kBK, kNST>;
 
-}  // namespace
-
-int qkv_block_tokens() { return CfgP<kWN, kWM, kMT, kBK, kNST>::BM; }
-
-hipError_t launch_qkv(const QkvArgs& a, hipStream_t stream) {
-  using C = CfgP<kWN, kWM, kMT, kBK, kNST>;
-  const int nM = (a.T + C::BM - 1) / C::BM;
+template <typename C, int MT>
+hipError_t launch_part(const QkvArgs& a, hipStream_t stream) {
+  const int nM = (a.T - a.m_begin + C::BM - 1) / C::BM;
   const int nN = (a.Hq + 2 * a.Hkv + kWN - 1) / kWN;
   const int total = nM * nN;
   const int grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((qkv_kernel<kWN, kWM, kMT, kBK, kNST>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((qkv_kernel<kWN, kWM, MT, kBK, kNST>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+int qkv_block_tokens() { return Main::BM; }
+
+// One workgroup runs per CU at a time. The 256-token tiles take the tokens that fill whole
+// rounds of the CUs; the tokens left over (which would run a last, mostly idle round) go to
+// half-height tiles, twice as many and each half as long.
+hipError_t launch_qkv(const QkvArgs& a, int n_cus, hipStream_t stream) {
+  const int nN = (a.Hq + 2 * a.Hkv + kWN - 1) / kWN;
+  const int full = a.T / Main::BM;                         // whole 256-token tiles
+  const int rounds = n_cus > 0 ? full * nN / n_cus : 0;    // whole rounds they fill
+  const int m_main = rounds * n_cus / nN;                  // token tiles of those rounds
+  QkvArgs p = a;
+  if (m_main > 0) {
+    p.m_begin = 0;
+    p.T = m_main * Main::BM;
+    const hipError_t e = launch_part<Main, 2>(p, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (m_main * Main::BM < a.T) {
+    p = a;
+    p.m_begin = m_main * Main::BM;
+    return launch_part<Tail, 1>(p, stream);
+  }
+  return hipSuccess;
 }
 
 }  // namespace ha
