@@ -178,9 +178,8 @@ __global__ __launch_bounds__((CfgP<WN, WM, MT, BK, NST>::NT), 1) void qkv_kernel
           acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[nt], bf[mt], acc[nt][mt], 0, 0, 0);
     }
   };
-  // The stage's DMA is issued before the products of an earlier stage; the scheduling
-  // barrier keeps the compiler from sinking it to the end of the step, where the next
-  // wait would expose its whole latency.
+  // Prologue DMA of a stage (in the loop, each step places its DMA between its products).
+  // The scheduling barrier keeps the compiler from sinking it behind the first products.
   auto fetch = [&](int t, char* xb, char* wb) __attribute__((always_inline)) {
     stage_dma<C, C::XI>(xg, K, m0, a.T - 1, t * BK, xb, wave, lane);
     stage_dma<C, C::WI>(wg, K, f0, nfeat - 1, t * BK, wb, wave, lane);
@@ -214,8 +213,23 @@ __global__ __launch_bounds__((CfgP<WN, WM, MT, BK, NST>::NT), 1) void qkv_kernel
     constexpr int JN = (J + NST - 1) % NST;
     wait_vm<C::IPW * (NST - 2)>();
     lds_barrier();
-    fetch(min(t + NST - 1, nks - 1), xbuf(std::integral_constant<int, JN>{}), wbuf(std::integral_constant<int, JN>{}));
+    {
+      const int tn = min(t + NST - 1, nks - 1);
+      stage_dma<C, C::XI>(xg, K, m0, a.T - 1, tn * BK, xbuf(std::integral_constant<int, JN>{}), wave, lane);
+      stage_dma<C, C::WI>(wg, K, f0, nfeat - 1, tn * BK, wbuf(std::integral_constant<int, JN>{}), wave, lane);
+    }
     compute(xbuf(j), wbuf(j));
+    // schedule per 16-k substep: its LDS reads, then its MFMAs with the stage's DMA spread
+    // between them (a burst of DMA ahead of the products stalls issue longer)
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 + MT, 0);  // DS reads of the substep
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // VMEM: stage DMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT - 4, 0);
+    }
   };
   fetch(0, x0, w0);
   fetch(min(1, nks - 1), x1, w1);
