@@ -162,7 +162,9 @@ ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
 
 /* Workspace bytes ha_attn_fwd needs: row limits, tile ranges, and the rotated q and k
  * when pro is not NULL; with HA_SEG_GEN segments also per-key visibility and per query
- * block tile lists. */
+ * block tile lists; with a split plan (below) its work item table and fp32 partial
+ * results. The plan depends on the current device's CU count, so call this with the
+ * device current that will run the forward. */
 size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro);
 
 /* Attention on prepared inputs: q and k already normalised and rotated (q optionally
@@ -180,7 +182,19 @@ ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const voi
 /* The whole path: classifier, prologue (skipped when pro is NULL: q, k are then used as
  * given), attention. With a prologue, the q it writes to the workspace is prescaled (its
  * q_out_scale is ignored) and desc->q_prescaled is ignored. workspace: DEVICE, 256-byte
- * aligned, >= ha_attn_workspace_bytes. */
+ * aligned, >= ha_attn_workspace_bytes.
+ *
+ * Split plan (bf16): where the heaviest query blocks would leave the CUs partly idle in
+ * their last round (e.g. the HunyuanImage 3.0 interleave, or fewer blocks than CUs), the
+ * host splits some blocks' key tiles into parts that run as separate work items and a
+ * merge kernel combines them (the merge rounds differently from one work item: results
+ * agree within bf16 rounding, not bit for bit, with ha_attn_fwd_planned). The work item
+ * table goes to the workspace by an asynchronous copy from pinned host memory that the
+ * library allocates once per distinct table (at most 256, kept until the process ends).
+ * A workspace smaller than ha_attn_workspace_bytes but large enough without the plan runs
+ * without it. Environment, read at each call: HA_SPLIT_PARTS=1 disables the plan,
+ * HA_SPLIT_PARTS=P > 1 splits every block into P parts, HA_CU_COUNT=n plans for n CUs
+ * (the last two for tests). */
 ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
                       const void* k, const void* v, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);

@@ -2,6 +2,9 @@
 inputs, and compare with the oracle at the stated tolerances."""
 from __future__ import annotations
 
+import contextlib
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,6 +17,28 @@ from workloads.device import to_device
 # Tolerances: bf16 inputs, max |err| <= 2e-2 and mean |err| <= 2e-3 against the oracle;
 # fp32 inputs, max |err| <= 1e-5 * max |oracle| over the whole output.
 BF16_MAX, BF16_MEAN, F32_REL = 2e-2, 2e-3, 1e-5
+
+
+@contextlib.contextmanager
+def env(**kv):
+    """Set environment variables the library reads at each call (HA_SPLIT_PARTS,
+    HA_CU_COUNT) for the duration of a block."""
+    old = {k: os.environ.get(k) for k in kv}
+    os.environ.update({k: str(v) for k, v in kv.items()})
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def unsplit():
+    """The bf16 forward without split query blocks: one work item per query block, the
+    summation order of ha_attn_fwd_planned."""
+    return env(HA_SPLIT_PARTS=1)
 
 
 def require_gpu():

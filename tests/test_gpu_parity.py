@@ -10,7 +10,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_helpers import (compare, desc_for, f64, prologue_for, refresh_bits, require_gpu,
-                         run_fwd, sample_rows)
+                         run_fwd, sample_rows, unsplit)
 from unified_text_pixel_amd import api, binding as B
 from workloads.device import to_device
 
@@ -361,7 +361,10 @@ def test_deterministic_and_fwd_equals_planned(name):
     a, dev = run_fwd(x)
     b, _ = run_fwd(x, dev)
     assert torch.equal(a, b)
-    # ha_attn_fwd writes a prescaled q to its workspace: the same as the planned path
+    # ha_attn_fwd writes a prescaled q to its workspace: the same as the planned path (with
+    # one work item per query block, as the planned path has)
+    with unsplit():
+        a, _ = run_fwd(x, dev)
     assert torch.equal(planned(x, dev, True), a)
     # plain q through the planned path: a different kernel variant, same result
     compare(f64(planned(x, dev, False)), oracle.hot_path(x), w.dtype, name + " planned plain q")

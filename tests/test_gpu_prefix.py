@@ -5,15 +5,16 @@ denoising steps its prologue outputs and attention outputs stay the same; only t
 after it need recomputing. Modelled here as two steps: step 0 runs the whole path; for step
 1 the tokens after the prefix get new q, k, v, and only ha_qk_prologue_from and
 ha_attn_fwd_planned_from run from the prefix end on the buffers step 0 left. The result must
-equal, bit for bit, a whole-path run on the step-1 inputs (the same kernels over the same
-values), and match the oracle on the step-1 inputs within the bf16 gates."""
+equal, bit for bit, a whole-path run on the step-1 inputs with one work item per query block
+(the same kernels over the same values; where ha_attn_fwd splits query blocks into parts, its
+merge rounds differently), and match the oracle on the step-1 inputs within the bf16 gates."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import compare, f64, refresh_bits, require_gpu, run_fwd
+from gpu_helpers import compare, f64, refresh_bits, require_gpu, run_fwd, unsplit
 from unified_text_pixel_amd import api, binding as B
 from workloads.device import to_device
 
@@ -63,7 +64,8 @@ def two_steps(w, p, row_begin=None):
         dev[n][:, p:] = dev1[n][:, p:]
     B.ha_qk_prologue_from(desc, pro, dev["q"], dev["k"], qr, kr, p)
     B.ha_attn_fwd_planned_from(desc, qr, kr, dev["v"], lim, ranges, out, row_begin)
-    whole, _ = run_fwd(x, dev1)
+    with unsplit():
+        whole, _ = run_fwd(x, dev1)
     torch.cuda.synchronize()
     return out, whole, x
 
@@ -108,8 +110,8 @@ def test_rows_before_row_begin_untouched():
 @pytest.mark.parametrize("rope,norm", [("mrope", True), ("none", False)])
 def test_api_forward_from_over_steps(rope, norm):
     """HybridAttention.forward_from over three denoising steps, each with new tokens after
-    the text, equals the whole forward of that step's inputs; begin inside the generation
-    grid is refused."""
+    the text, equals the whole forward of that step's inputs (one work item per query
+    block); begin inside the generation grid is refused."""
     w = hidream(66, 12, seed=47).replace(rope=rope, qk_norm=norm)
     x = W.generate(w)
     dev = to_device(x)
@@ -125,7 +127,8 @@ def test_api_forward_from_over_steps(rope, norm):
             for t in (q, k, v):
                 t[:, 66:] = torch.randn(t[:, 66:].shape, generator=gen, device="cuda").to(t.dtype)
         got = attn.forward_from(q, k, v, 66 if step else 0)
-        want = attn(q, k, v)
+        with unsplit():
+            want = attn(q, k, v)
         torch.cuda.synchronize()
         assert torch.equal(got, want), f"step {step}"
     with pytest.raises(ValueError):

@@ -1,0 +1,166 @@
+"""Split query blocks in the bf16 forward (ha_attn_fwd, ha_attn_fwd_lse): the work items may
+split a query block's tile list into parts, each writing an unnormalised partial output, row
+sum and row reference that a merge kernel combines. The planner splits only where the heavy
+blocks leave a CU round partly idle (the HunyuanImage layouts on 256 CUs); two environment
+variables, read at each call, reach the other cases: HA_SPLIT_PARTS=P splits every block into
+P parts (P = 1 never splits) and HA_CU_COUNT plans for another CU count.
+
+Each case is checked against the oracle at the usual tolerances and against the unsplit run
+(same inputs; the two differ only in the fp32 summation order before the bf16 rounding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import (compare, desc_for, env, f64, prologue_for, refresh_bits, require_gpu,
+                         run_fwd, sample_rows)
+from test_gpu_parity import SMALL, small
+from unified_text_pixel_amd import binding as B
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+C, F, G, GEN = W.SEG_CAUSAL, W.SEG_FULL, W.SEG_GCA, W.SEG_GEN
+LSE_ABS = 2e-2  # as for the training forward
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def fwd_lse(x, dev):
+    """ha_attn_fwd_lse (ha_attn_fwd and no lse for GQA groups of 8, which the training entry
+    points do not take); returns (out, lse or None, workspace bytes)."""
+    w = x.workload
+    desc = desc_for(w, x.segments)
+    pro = prologue_for(w, dev)
+    nbytes = B.ha_attn_workspace_bytes(desc, pro)
+    ws = torch.empty(max(256, nbytes), dtype=torch.uint8, device="cuda")
+    out = torch.full_like(dev["q"], float("nan"))
+    if w.n_q_heads // w.n_kv_heads > 4:
+        B.ha_attn_fwd(desc, pro, dev["q"], dev["k"], dev["v"], out, ws)
+        torch.cuda.synchronize()
+        return out, None, nbytes
+    lse = torch.full((w.batch, w.n_q_heads, w.seq_len), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    B.ha_attn_fwd_lse(desc, pro, dev["q"], dev["k"], dev["v"], out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse, nbytes
+
+
+def close_to_unsplit(got, ref, what):
+    """Same inputs, another fp32 summation order: at most a couple of bf16 ulps apart."""
+    a, b = f64(got), f64(ref)
+    tol = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 2.0 ** -14
+    bad = np.abs(a - b) > tol
+    print(f"{what}: max|split - unsplit| {np.abs(a - b).max():.3e}", flush=True)
+    assert not bad.any(), (what, int(bad.sum()))
+
+
+FORCED = ["hd_small", "edit_small", "gca_small", "gqa_g8", "mha_g1", "d64_bf16", "one_token",
+          "causal_rows_in_long_block", "all_full", "gen_small", "gen_first", "gen_adjacent",
+          "gen_g1_d64"]
+
+
+@pytest.mark.parametrize("parts", [2, 5])
+@pytest.mark.parametrize("name", FORCED)
+def test_forced_split_small(name, parts):
+    """Every block in 2 or 5 parts: parts of one tile, empty parts (5 parts of blocks with
+    fewer tiles), masked tiles in any part, Gen Image holes; output and lse against the
+    oracle and against the unsplit run."""
+    w = SMALL[name]
+    print(f"case {name}: parts {parts} S={w.seq_len}", flush=True)
+    x = W.generate(w)
+    dev = to_device(x)
+    with env(HA_SPLIT_PARTS=1):
+        ref, ref_lse, n0 = fwd_lse(x, dev)
+    with env(HA_SPLIT_PARTS=parts):
+        out, lse, n1 = fwd_lse(x, dev)
+        plain, _ = run_fwd(x, dev)
+    assert n1 > n0, "the split plan was not taken"
+    compare(f64(out), oracle.hot_path(x), "bf16", f"{name} in {parts} parts")
+    close_to_unsplit(out, ref, name)
+    assert torch.equal(plain, out), "ha_attn_fwd and ha_attn_fwd_lse differ on the split path"
+    if lse is not None:
+        err = float(np.abs(f64(lse) - oracle.path_lse(x)).max())
+        print(f"{name}: lse max|err| {err:.3e}", flush=True)
+        assert err <= LSE_ABS, err
+        assert float((lse - ref_lse).abs().max()) <= 1e-4
+
+
+@pytest.mark.parametrize("alpha,sign", [(26.0, 1.0), (36.0, -1.0)])
+def test_forced_split_careful_pass(alpha, sign):
+    """Scores shifted by +86 or -165 log2 units: the parts take the careful re-referencing
+    pass, so the merge combines partial results on different references."""
+    w = small([W.Segment(C, 40), W.Segment(F, 100), W.Segment(G, 61)], rope="none", norm=False,
+              hq=8, hkv=2)
+    x = W.generate(w)
+    x.q[..., 0] += sign * alpha
+    x.k[..., 0] += alpha
+    refresh_bits(x)
+    dev = to_device(x)
+    with env(HA_SPLIT_PARTS=3):
+        out, _ = run_fwd(x, dev)
+    compare(f64(out), oracle.hot_path(x), "bf16", f"split, extreme logits {sign * alpha}")
+
+
+def test_forced_split_late_keys_one_head():
+    """Only head 3 and keys from 130 on carry the shift: in a split block some parts take the
+    careful pass and others do not."""
+    w = small([W.Segment(C, 40), W.Segment(F, 100), W.Segment(G, 61)], rope="none", norm=False,
+              hq=8, hkv=2)
+    x = W.generate(w)
+    x.q[:, :, 3, 0] += 26.0
+    x.k[:, 130:, :, 0] += 26.0
+    refresh_bits(x)
+    dev = to_device(x)
+    with env(HA_SPLIT_PARTS=2):
+        out, _ = run_fwd(x, dev)
+    compare(f64(out), oracle.hot_path(x), "bf16", "split, late extreme keys in one head")
+
+
+@pytest.mark.parametrize("name,cus", [("hunyuan", None), ("hunyuan_multigen", 240),
+                                      ("hunyuan", 240), ("hd2048", 240), ("hd2048", 304)])
+def test_planner_full_size(name, cus):
+    """The planner on full-size layouts, for this device's CU count (None) or another one:
+    sampled rows against the oracle, every output and lse against the unsplit run."""
+    w = W.get_config(name)
+    print(f"case {name}: cus {cus}", flush=True)
+    x = W.generate(w)
+    dev = to_device(x)
+    with env(HA_SPLIT_PARTS=1):
+        ref, ref_lse, n0 = fwd_lse(x, dev)
+    with env(**({"HA_CU_COUNT": cus} if cus else {})):
+        out, lse, n1 = fwd_lse(x, dev)
+    if cus is None and n1 == n0:
+        pytest.skip("this device's CU count gives no split for this layout")
+    assert n1 > n0, "the split plan was not taken"
+    got = f64(out)
+    rows = sample_rows(w)
+    for b in range(w.batch):
+        want = oracle.hot_path_rows(x, b, rows, list(range(w.n_q_heads)))
+        compare(got[b, rows], want, w.dtype, f"{name} batch {b}, split")
+    close_to_unsplit(out, ref, name)
+    assert float((lse - ref_lse).abs().max()) <= 1e-4
+
+
+def test_split_with_short_workspace_runs_unsplit():
+    """A workspace sized for the unsplit path (smaller than ha_attn_workspace_bytes asks for
+    with a split plan) runs unsplit rather than failing."""
+    w = SMALL["gca_small"]
+    x = W.generate(w)
+    dev = to_device(x)
+    desc = desc_for(w, x.segments)
+    pro = prologue_for(w, dev)
+    with env(HA_SPLIT_PARTS=1):
+        n0 = B.ha_attn_workspace_bytes(desc, pro)
+        ref, _ = run_fwd(x, dev)
+    with env(HA_SPLIT_PARTS=4):
+        assert B.ha_attn_workspace_bytes(desc, pro) > n0
+        ws = torch.empty(n0, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(dev["q"])
+        B.ha_attn_fwd(desc, pro, dev["q"], dev["k"], dev["v"], out, ws)
+        torch.cuda.synchronize()
+    assert torch.equal(out, ref)

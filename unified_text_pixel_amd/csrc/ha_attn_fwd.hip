@@ -201,11 +201,17 @@ struct Dma {
   }
 };
 
-// HOLE: a layout with Gen Images. The work item walks its query block's tile list
-// (inside FULL tiles first, then the rest) instead of tiles [0, kend), and masked tiles
-// also hide keys whose visibility ends at or before the row.
-template <int D, int G, bool PRE, bool LSE, bool HOLE>
+// LM, the list mode: 0, the work item walks tiles [0, kend) of its query block, tile t at
+// position t.
+//   LM & 1  (a layout with Gen Images) it walks the query block's tile list instead (inside
+//           FULL tiles first, then the rest), and masked tiles also hide keys whose
+//           visibility ends at or before the row;
+//   LM & 2  work items come from a table: a query block may be split into parts, each
+//           walking a share of the positions and writing unnormalised partial results that
+//           combine_kernel merges.
+template <int D, int G, bool PRE, bool LSE, int LM>
 __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
+  constexpr bool KVIS = (LM & 1) != 0, ITEMS = (LM & 2) != 0, LIST = KVIS;
   using C = CfgB<D, G>;
   using TL = Tile<D>;
   // K and V double buffers as four distinct arrays: a read of one buffer then never waits
@@ -216,8 +222,23 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char v1[TL::BYTES];
   __shared__ int redo;  // some row left the range on the main pass: redo the work item
 
-  const Item it = work_item(a);
-  const int b = it.b, g = it.g, qb = it.qb;
+  int b, g, qb, part = 0, nparts = 1, slot = -1;
+  if constexpr (ITEMS) {
+    const int32_t* itm = a.items + (int64_t)blockIdx.x * 4;
+    const int bg = itm[0];
+    if (bg < 0) return;  // padding entry: the whole workgroup leaves before any barrier
+    b = bg / a.Hkv;
+    g = bg % a.Hkv;
+    qb = itm[1];
+    part = itm[2] & 0xffff;
+    nparts = itm[2] >> 16;
+    slot = itm[3];
+  } else {
+    const Item it = work_item(a);
+    b = it.b;
+    g = it.g;
+    qb = it.qb;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave % G, tsub = wave / G;
@@ -231,13 +252,31 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : S;
   // positions [0, kfull) of the walk are unmasked, [kfull, kend) masked; position t is
   // key tile tile_at(t)
-  const int32_t* cnt = HOLE ? a.tile_count : a.ranges;
-  const int kfull = cnt[((int64_t)b * a.nq + qb) * 2 + 0];
-  const int kend = cnt[((int64_t)b * a.nq + qb) * 2 + 1];
-  const int32_t* tlist = HOLE ? a.tiles + ((int64_t)b * a.nq + qb) * a.nk : nullptr;
+  const int32_t* cnt = LIST ? a.tile_count : a.ranges;
+  int kfull = cnt[((int64_t)b * a.nq + qb) * 2 + 0];
+  int kend = cnt[((int64_t)b * a.nq + qb) * 2 + 1];
+  const int32_t* tlist = LIST ? a.tiles + ((int64_t)b * a.nq + qb) * a.nk : nullptr;
+  int t0 = 0;  // tile at position 0 (without a list)
+  if constexpr (ITEMS) {
+    if (nparts > 1) {  // part p of the walk: positions [p n / P, (p + 1) n / P)
+      const int p0 = (int)((int64_t)part * kend / nparts), p1 = (int)((int64_t)(part + 1) * kend / nparts);
+      if constexpr (LIST)
+        tlist += p0;
+      else
+        t0 = p0;
+      kfull = min(max(kfull - p0, 0), p1 - p0);
+      kend = p1 - p0;
+    }
+    if (kend <= 0) {  // an empty part: it saw no key (the merge skips it)
+      if (hi == 0) a.part_l[((int64_t)slot * C::BQ + tsub * 32 + (lane & 31)) * G + hg] = 0.f;
+      return;
+    }
+  }
   auto tile_at = [&](int t) __attribute__((always_inline)) {
-    if constexpr (HOLE)
+    if constexpr (LIST)
       return tlist[t];
+    else if constexpr (ITEMS)
+      return t0 + t;
     else
       return t;
   };
@@ -295,7 +334,7 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   auto mask = [&](f32x16 (&sc)[2], int t) {
     const int tile = tile_at(t);
     if (t < kfull && (tile + 1) * BK <= S) return;
-    if constexpr (HOLE) {
+    if constexpr (KVIS) {
       // the lane's keys come in runs of 4: key_vis rows are padded, so every run is in bounds
       const int* kv = a.key_vis + (int64_t)b * a.kv_stride + tile * BK + 4 * hi;
 #pragma unroll
@@ -387,7 +426,7 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // so is tile t + 2 (DMA without clamping). Both loops take two steps per trip (odd t,
   // then even), the S registers alternating roles; sb holds S_t when a trip starts. (A
   // tile list puts the tiles that are full and inside the sequence first.)
-  const int fast_end = HOLE ? max(1, min(kfull, kend) - 2) : max(1, min(min(kfull, kend - 2), S / BK - 2));
+  const int fast_end = LIST ? max(1, min(kfull, kend) - 2) : max(1, min(min(kfull, kend - 2), S / BK - t0 - 2));
   step(std::false_type{}, P0{}, 0, sa, sb, pb, pa);  // S_1 -> sb, P_0 -> pa
   int t = 1;
   for (; t + 1 < fast_end; t += 2) {
@@ -463,6 +502,24 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     }
   }
 
+  // a part of a split query block: its unnormalised output, row sum and row reference
+  if constexpr (ITEMS) {
+    if (slot >= 0) {
+      const int64_t r = (int64_t)slot * C::BQ + tsub * 32 + (lane & 31);
+      float* po = a.part_o + (r * G + hg) * D;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(po + 32 * mt + 8 * j + 4 * hi) =
+              f32x4{o[mt][4 * j], o[mt][4 * j + 1], o[mt][4 * j + 2], o[mt][4 * j + 3]};
+      if (hi == 0) {
+        a.part_l[r * G + hg] = l;
+        a.part_m[r * G + hg] = mref;
+      }
+      return;
+    }
+  }
   // row log-sum-exp of the natural-unit scores for a training backward: with the scores in
   // log2 units, log2 sum_j 2^s_j = m + log2(l)
   if constexpr (LSE) {
@@ -596,24 +653,24 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
 }
 
 // ====================================================================== launch
-template <int D, int G, bool HOLE>
+template <int D, int G, int LM>
 void launch_bf16(const AttnArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(CfgB<D, G>::NT);
   if (a.lse) {
     if (a.q_prescaled)
-      hipLaunchKernelGGL((attn_bf16<D, G, true, true, HOLE>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16<D, G, true, true, LM>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_bf16<D, G, false, true, HOLE>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16<D, G, false, true, LM>), grid, block, 0, stream, a);
   } else if (a.q_prescaled) {
-    hipLaunchKernelGGL((attn_bf16<D, G, true, false, HOLE>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16<D, G, true, false, LM>), grid, block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_bf16<D, G, false, false, HOLE>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16<D, G, false, false, LM>), grid, block, 0, stream, a);
   }
 }
 
 template <int D, int G>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-  const int64_t items = (int64_t)a.B * a.Hkv * a.nq_run;
+  const int64_t items = a.items ? a.n_items : (int64_t)a.B * a.Hkv * a.nq_run;
   const dim3 grid((unsigned)items);
   if (a.f32) {
     const dim3 block(CfgF<D, G>::NT);
@@ -622,10 +679,14 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((attn_f32<D, G, false>), grid, block, 0, stream, a);
   } else {
-    if (a.tiles)
-      launch_bf16<D, G, true>(a, grid, stream);
-    else
-      launch_bf16<D, G, false>(a, grid, stream);
+    // list mode: key visibility with Gen Images, an item table for split query blocks
+    const int lm = (a.key_vis ? 1 : 0) | (a.items ? 2 : 0);
+    switch (lm) {
+      case 1: launch_bf16<D, G, 1>(a, grid, stream); break;
+      case 2: launch_bf16<D, G, 2>(a, grid, stream); break;
+      case 3: launch_bf16<D, G, 3>(a, grid, stream); break;
+      default: launch_bf16<D, G, 0>(a, grid, stream); break;
+    }
   }
   return hipGetLastError();
 }
@@ -649,6 +710,64 @@ int attn_block_q(int head_dim, int group, bool f32) {
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   return a.D == 128 ? launch_g<128>(a, stream) : launch_g<64>(a, stream);
+}
+
+// ====================================================================== merge of split parts
+// A query block split into P parts has, per row and head, P unnormalised outputs O_p, row
+// sums l_p and references m_p (log2 units: the part's exponentials are exp2(s - m_p)).
+// With M = max m_p over the parts that saw a key (l_p > 0) and w_p = exp2(m_p - M):
+//   out = sum_p w_p O_p / sum_p w_p l_p,   lse = ln 2 (M + log2 sum_p w_p l_p).
+// Threads: one per (row, head, 8 output dims); split blocks in blockIdx.y.
+namespace {
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int32_t* sp = a.splits + (int64_t)blockIdx.y * 4;
+  const int bg = sp[0], qb = sp[1], s0 = sp[2], np = sp[3];
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // (row, head, chunk of 8 dims)
+  constexpr int CH = D / 8;
+  if (idx >= a.BQ * a.G * CH) return;
+  const int ch = idx % CH, hg = (idx / CH) % a.G, r = idx / (CH * a.G);
+  const int i = a.S - (a.nq - qb) * a.BQ + r;
+  if (i < 0) return;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) {
+    const int64_t e = ((int64_t)(s0 + p) * a.BQ + r) * a.G + hg;
+    if (a.part_l[e] > 0.f) M = fmaxf(M, a.part_m[e]);
+  }
+  float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < np; ++p) {
+    const int64_t e = ((int64_t)(s0 + p) * a.BQ + r) * a.G + hg;
+    const float lp = a.part_l[e];
+    if (!(lp > 0.f)) continue;
+    const float w = __builtin_amdgcn_exp2f(a.part_m[e] - M);
+    L += w * lp;
+    const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + e * D + 8 * ch);
+    const f32x4 u = po[0], v = po[1];
+    for (int k = 0; k < 4; ++k) {
+      acc[k] += w * u[k];
+      acc[4 + k] += w * v[k];
+    }
+  }
+  const float inv = 1.f / L;
+  const int h = g * a.G + hg;
+  __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.S + i) * a.Hq + h) * D + 8 * ch;
+  bf16x8 o;
+  for (int k = 0; k < 8; ++k) o[k] = static_cast<__bf16>(acc[k] * inv);
+  *reinterpret_cast<bf16x8*>(orow) = o;
+  if (a.lse && ch == 0) a.lse[((int64_t)b * a.Hq + h) * a.S + i] = (M + __builtin_amdgcn_logf(L)) * 0.693147180559945309f;
+}
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  if (a.n_splits == 0) return hipSuccess;
+  const int threads = a.BQ * a.G * (a.D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)a.n_splits);
+  if (a.D == 128)
+    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace ha

@@ -14,7 +14,11 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <mutex>
+#include <queue>
 #include <string>
+#include <vector>
 
 #include "ha_internal.h"
 
@@ -263,9 +267,18 @@ ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const v
   return check_launch(ha::launch_prologue(a, stream), stream, "prologue");
 }
 
+// split query blocks on the device (null items: one work item per query block)
+struct SplitRun {
+  const int32_t* items = nullptr;
+  int n_items = 0;
+  float* part_o = nullptr;
+  float* part_l = nullptr;
+  float* part_m = nullptr;
+};
+
 ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const void* v, const int32_t* row_limit,
                    const int32_t* ranges, void* out, bool prescaled, hipStream_t stream, float* lse = nullptr,
-                   int row_begin = 0, const HolePlan& hole = HolePlan{}) {
+                   int row_begin = 0, const HolePlan& hole = HolePlan{}, const SplitRun& split = SplitRun{}) {
   ha::AttnArgs a{};
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
@@ -294,11 +307,221 @@ ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const vo
   a.tile_count = hole.tile_count;
   a.kv_stride = ha::key_vis_stride(d->seq_len);
   a.nk = nk;
+  a.items = split.items;
+  a.n_items = split.n_items;
+  a.part_o = split.part_o;
+  a.part_l = split.part_l;
+  a.part_m = split.part_m;
   return check_launch(ha::launch_attn(a, stream), stream, "attention");
+}
+
+// ---------------------------------------------------------------- split query blocks
+// Load balance of the bf16 forward (the workspace entry points). One work item per (batch,
+// KV head, query block) can leave the CUs idle: with the HunyuanImage interleave each XCD
+// serves one (batch, KV head) pair, 66 blocks of ~92 tiles on 32 CUs, so two of them run
+// alone in a third round. The planner sorts each XCD's items by their tile count and splits
+// the heavy items past the last whole round into parts that walk shares of their key tiles;
+// it picks the part count by simulating list scheduling (the hardware dispatches in table
+// order to the CU that frees up first). A merge kernel combines the parts.
+
+// a positive integer from the environment, else 0
+int env_int(const char* name) {
+  const char* e = std::getenv(name);
+  const int v = e ? std::atoi(e) : 0;
+  return v > 0 ? v : 0;
+}
+
+// CUs of the current device (HA_CU_COUNT overrides it, for tests of the split path)
+int device_cus() {
+  if (const int v = env_int("HA_CU_COUNT")) return v;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+struct SplitPlan {
+  bool active = false;
+  int n_items = 0, n_slots = 0, n_splits = 0;
+  std::vector<int32_t> items;   // [n_items][4]: b * Hkv + g (or -1), block, part | parts << 16, slot
+  std::vector<int32_t> splits;  // [n_splits][4]: b * Hkv + g, block, first slot, parts
+};
+
+// The item and split tables reach the device by an asynchronous copy from pinned host
+// memory, which must outlive the copy: each distinct table is kept, unchanged, until the
+// process ends (a layout that repeats reuses its copy). Past kMaxTables distinct tables
+// the planner is not used (nullptr).
+constexpr size_t kMaxTables = 256;
+const int32_t* pinned_table(const std::vector<int32_t>& v) {
+  static std::mutex mu;
+  static std::vector<std::pair<std::vector<int32_t>, int32_t*>> kept;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : kept)
+    if (e.first == v) return e.second;
+  if (kept.size() >= kMaxTables) return nullptr;
+  void* p = nullptr;
+  if (hipHostMalloc(&p, std::max<size_t>(v.size(), 1) * 4, hipHostMallocDefault) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::memcpy(p, v.data(), v.size() * 4);
+  kept.emplace_back(v, static_cast<int32_t*>(p));
+  return kept.back().second;
+}
+
+// Key tiles each query block of batch item b executes, from the segment table: the tiles
+// before its rows' largest key limit, less, with Gen Images, the tiles whose every key is
+// hidden from the block's first row (the tile classifier's SKIP rule).
+std::vector<int> block_costs(const ha_attn_desc* d, int b, int bq, int nq, int nk) {
+  const int S = d->seq_len, bk = ha::kBlockK;
+  const ha_segment* seg = d->segments + (int64_t)b * d->n_segments;
+  std::vector<int> vmax;  // per key tile: the largest visibility end of its keys
+  if (has_gen(d)) {
+    vmax.assign(nk, 0);
+    for (int s = 0; s < d->n_segments; ++s) {
+      const int st = seg[s].start, en = st + seg[s].length;
+      for (int kb = st / bk; kb < nk && kb * bk < en; ++kb)
+        vmax[kb] = std::max(vmax[kb], seg[s].kind == HA_SEG_GEN ? en : S);
+    }
+  }
+  std::vector<int> cost(nq);
+  for (int qb = 0; qb < nq; ++qb) {
+    const int r1 = S - (nq - 1 - qb) * bq, r0 = std::max(0, r1 - bq);
+    int lmax = 0;
+    for (int s = 0; s < d->n_segments; ++s) {
+      const int st = seg[s].start, en = st + seg[s].length;
+      if (en <= r0 || st >= r1) continue;
+      lmax = std::max(lmax, seg[s].kind == HA_SEG_CAUSAL ? std::min(en, r1) : (seg[s].kind == HA_SEG_FULL ? S : en));
+    }
+    const int kend = (lmax + bk - 1) / bk;
+    int n = kend;
+    if (!vmax.empty())
+      for (int kb = 0; kb < kend; ++kb) n -= vmax[kb] <= r0 ? 1 : 0;
+    cost[qb] = n;
+  }
+  return cost;
+}
+
+// makespan of list scheduling in the given order on n machines
+double list_schedule(const std::vector<double>& costs, int n) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> q;
+  for (int i = 0; i < n; ++i) q.push(0.0);
+  double ms = 0.0;
+  for (double c : costs) {
+    double t = q.top();
+    q.pop();
+    t += c;
+    ms = std::max(ms, t);
+    q.push(t);
+  }
+  return ms;
+}
+
+// HA_SPLIT_PARTS (for tests): 1 never splits, P > 1 splits every query block into P parts.
+SplitPlan plan_split(const ha_attn_desc* d) {
+  SplitPlan plan;
+  if (d->dtype != HA_DTYPE_BF16 || empty(d)) return plan;
+  const int force = std::min(env_int("HA_SPLIT_PARTS"), 64);
+  if (force == 1) return plan;
+  const int n_cus = device_cus();
+  if (n_cus <= 0) return plan;
+  int bq, bk, nq, nk;
+  tile_shape(d, &bq, &bk, &nq, &nk);
+  const int nbg = d->batch * d->n_kv_heads;
+  const bool affine = nbg % 8 == 0;  // the unsplit order keeps each pair on one XCD
+  const int groups = affine ? 8 : 1;
+  const int cus = std::max(1, affine ? n_cus / 8 : n_cus);
+  constexpr double kItem = 4.0;  // fixed cost of a work item (start, last tile, stores), in tiles
+  struct E {
+    int bg, qb, cost, part, parts, slot;
+  };
+  std::vector<std::vector<E>> lists(groups);
+  std::vector<int> cost;  // of batch item cost_b
+  int cost_b = -1;
+  int slot = 0;
+  for (int x = 0; x < groups; ++x) {
+    std::vector<E> it;
+    for (int bg = affine ? x : 0; bg < nbg; bg += affine ? 8 : 1) {
+      const int b = bg / d->n_kv_heads;
+      if (b != cost_b) {
+        cost = block_costs(d, b, bq, nq, nk);
+        cost_b = b;
+      }
+      for (int qb = nq - 1; qb >= 0; --qb) it.push_back({bg, qb, cost[qb], 0, 1, -1});
+    }
+    std::stable_sort(it.begin(), it.end(), [](const E& p, const E& q) { return p.cost > q.cost; });
+    if (it.empty()) continue;
+    const int cmax = it[0].cost;
+    int heavy = 0;
+    while (heavy < (int)it.size() && 4 * it[heavy].cost >= 3 * cmax) ++heavy;
+    int k = heavy / cus * cus;  // the heavy items that fill whole rounds stay whole
+    if (force > 1) {
+      k = 0;
+      heavy = (int)it.size();
+    }
+    int best = 1;
+    double best_ms = 0.0, whole_ms = 0.0;
+    for (int parts : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
+      if (force > 1 || (parts > 1 && (k == heavy || parts > cmax))) break;
+      std::vector<double> c;
+      for (int i = 0; i < (int)it.size(); ++i) {
+        const bool split = parts > 1 && i >= k && i < heavy;
+        for (int p = 0; p < (split ? parts : 1); ++p)
+          c.push_back((split ? std::ceil((double)it[i].cost / parts) : (double)it[i].cost) + kItem);
+      }
+      std::stable_sort(c.begin(), c.end(), std::greater<double>());
+      const double ms = list_schedule(c, cus) + (parts > 1 ? kItem : 0.0);  // + the merge
+      if (parts == 1) whole_ms = ms;
+      if (parts == 1 || ms < best_ms) {
+        best = parts;
+        best_ms = ms;
+      }
+    }
+    if (best_ms > 0.97 * whole_ms) best = 1;  // not worth a merge
+    if (force > 1) best = force;
+    std::vector<E>& out = lists[x];
+    for (int i = 0; i < (int)it.size(); ++i) {
+      if (best > 1 && i >= k && i < heavy) {
+        plan.splits.insert(plan.splits.end(), {it[i].bg, it[i].qb, slot, best});
+        for (int p = 0; p < best; ++p)
+          out.push_back({it[i].bg, it[i].qb, (it[i].cost + best - 1) / best, p, best, slot + p});
+        slot += best;
+      } else {
+        out.push_back(it[i]);
+      }
+    }
+    std::stable_sort(out.begin(), out.end(), [](const E& p, const E& q) { return p.cost > q.cost; });
+  }
+  if (slot == 0) return plan;  // nothing to split: the unsplit order is as good
+  size_t longest = 0;
+  for (const auto& l : lists) longest = std::max(longest, l.size());
+  plan.n_items = (int)(longest * groups);
+  plan.items.assign((size_t)plan.n_items * 4, 0);
+  for (int i = 0; i < plan.n_items; ++i) {
+    const auto& l = lists[i % groups];
+    const size_t at = (size_t)(i / groups);
+    int32_t* e = &plan.items[(size_t)i * 4];
+    if (at < l.size()) {
+      e[0] = l[at].bg;
+      e[1] = l[at].qb;
+      e[2] = l[at].part | (l[at].parts << 16);
+      e[3] = l[at].slot;
+    } else {
+      e[0] = -1;  // padding
+    }
+  }
+  plan.n_slots = slot;
+  plan.n_splits = (int)(plan.splits.size() / 4);
+  plan.active = true;
+  return plan;
 }
 
 struct Workspace {
   size_t row_limit, ranges, q_rot, k_rot, key_vis, tiles, tile_count, total;
+  size_t items, part_o, part_l, part_m;  // split query blocks: items, then the split table
 };
 
 // Bytes of the Gen Image plan arrays, placed at *at (offsets into the workspace).
@@ -321,7 +544,7 @@ HolePlan hole_plan(const ha_attn_desc* d, char* ws, size_t key_vis, size_t tiles
   return h;
 }
 
-Workspace workspace_layout(const ha_attn_desc* d, bool prologue) {
+Workspace workspace_layout(const ha_attn_desc* d, bool prologue, const SplitPlan& split = SplitPlan{}) {
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
   const size_t elem = d->dtype == HA_DTYPE_F32 ? 4 : 2;
@@ -338,6 +561,17 @@ Workspace workspace_layout(const ha_attn_desc* d, bool prologue) {
     at = round256(at + (size_t)d->batch * d->seq_len * d->n_kv_heads * d->head_dim * elem);
   }
   if (has_gen(d)) take_hole(d, nq, nk, &at, &w.key_vis, &w.tiles, &w.tile_count);
+  if (split.active) {
+    const size_t G = d->n_q_heads / d->n_kv_heads;
+    auto take = [&](size_t& field, size_t bytes) {
+      field = at;
+      at = round256(at + bytes);
+    };
+    take(w.items, (size_t)(split.n_items + split.n_splits) * 16);
+    take(w.part_o, (size_t)split.n_slots * bq * G * d->head_dim * 4);
+    take(w.part_l, (size_t)split.n_slots * bq * G * 4);
+    take(w.part_m, (size_t)split.n_slots * bq * G * 4);
+  }
   w.total = at;
   return w;
 }
@@ -464,7 +698,7 @@ ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro, 
 
 size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro) {
   if (check_desc(desc) != HA_OK) return 0;
-  return workspace_layout(desc, pro != nullptr).total;
+  return workspace_layout(desc, pro != nullptr, plan_split(desc)).total;
 }
 
 ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const void* k, const void* v,
@@ -497,13 +731,38 @@ ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const 
   if ((st = check_tensor(q, "q")) != HA_OK || (st = check_tensor(k, "k")) != HA_OK ||
       (st = check_tensor(v, "v")) != HA_OK || (st = check_tensor(out, "out")) != HA_OK)
     return st;
-  const Workspace w = workspace_layout(desc, pro != nullptr);
+  // the split plan when the workspace holds it (the bytes that ha_attn_workspace_bytes
+  // gives), else one work item per query block
+  SplitPlan plan = plan_split(desc);
+  Workspace w = workspace_layout(desc, pro != nullptr, plan);
+  const int32_t* table = nullptr;
+  if (plan.active && workspace_bytes >= w.total) {
+    std::vector<int32_t> both = plan.items;
+    both.insert(both.end(), plan.splits.begin(), plan.splits.end());
+    table = pinned_table(both);
+  }
+  if (!table) {
+    plan = SplitPlan{};
+    w = workspace_layout(desc, pro != nullptr);
+  }
   if ((st = check_workspace(workspace, workspace_bytes, w.total)) != HA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   int32_t* row_limit = reinterpret_cast<int32_t*>(ws + w.row_limit);
   int32_t* ranges = reinterpret_cast<int32_t*>(ws + w.ranges);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const HolePlan hole = hole_plan(desc, ws, w.key_vis, w.tiles, w.tile_count);
+  SplitRun split;
+  if (plan.active) {
+    split.items = reinterpret_cast<int32_t*>(ws + w.items);
+    split.n_items = plan.n_items;
+    split.part_o = reinterpret_cast<float*>(ws + w.part_o);
+    split.part_l = reinterpret_cast<float*>(ws + w.part_l);
+    split.part_m = reinterpret_cast<float*>(ws + w.part_m);
+    const size_t bytes = (size_t)(plan.n_items + plan.n_splits) * 16;
+    if ((st = check_launch(hipMemcpyAsync(ws + w.items, table, bytes, hipMemcpyHostToDevice, s), s,
+                           "item table copy")) != HA_OK)
+      return st;
+  }
   if ((st = run_classify(desc, nullptr, ranges, row_limit, s, hole)) != HA_OK) return st;
   const void* qa = q;
   const void* ka = k;
@@ -514,7 +773,27 @@ ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const 
     qa = qr;
     ka = kr;
   }
-  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, pro != nullptr, s, lse, 0, hole);
+  st = run_attn(desc, qa, ka, v, row_limit, ranges, out, pro != nullptr, s, lse, 0, hole, split);
+  if (st == HA_OK && plan.active) {
+    ha::CombineArgs c{};
+    int bq, bk, nq, nk;
+    tile_shape(desc, &bq, &bk, &nq, &nk);
+    c.splits = split.items + (size_t)plan.n_items * 4;
+    c.part_o = split.part_o;
+    c.part_l = split.part_l;
+    c.part_m = split.part_m;
+    c.out = out;
+    c.lse = lse;
+    c.n_splits = plan.n_splits;
+    c.S = desc->seq_len;
+    c.Hq = desc->n_q_heads;
+    c.Hkv = desc->n_kv_heads;
+    c.nq = nq;
+    c.BQ = bq;
+    c.G = desc->n_q_heads / desc->n_kv_heads;
+    c.D = desc->head_dim;
+    st = check_launch(ha::launch_combine(c, s), s, "merge of split query blocks");
+  }
   return st == HA_OK ? ok() : st;
 }
 

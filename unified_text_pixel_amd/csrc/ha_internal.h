@@ -82,8 +82,29 @@ struct AttnArgs {
   const int32_t* tiles;
   const int32_t* tile_count;
   int32_t kv_stride, nk;
+  // split query blocks (bf16, else null): the work item table [n_items][4] of (b * Hkv + g,
+  // query block, part | parts << 16, partial slot or -1) and the partial outputs per slot:
+  // part_o [slot][BQ][G][D], part_l and part_m [slot][BQ][G]
+  const int32_t* items;
+  int32_t n_items;
+  float* part_o;
+  float* part_l;
+  float* part_m;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+// Merge of split query blocks: splits [n_splits][4] of (b * Hkv + g, query block, first
+// slot, parts); writes out (bf16) and, when lse is set, the row lse.
+struct CombineArgs {
+  const int32_t* splits;
+  const float* part_o;
+  const float* part_l;
+  const float* part_m;
+  void* out;
+  float* lse;
+  int32_t n_splits, S, Hq, Hkv, nq, BQ, G, D;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 // ---- QKV projection with the prologue in its epilogue (ha_qkv.hip)
 struct QkvArgs {
