@@ -461,7 +461,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
   const int32_t* tlist = HOLE ? a.tiles + ((int64_t)b * nq + qb) * a.nk : nullptr;
   auto tile_at = [&](int t) __attribute__((always_inline)) {
     if constexpr (HOLE)
-      return tlist[t];
+      return ((const __attribute__((address_space(4))) int32_t*)tlist)[t];  // scalar loads (written before the launch)
     else
       return t;
   };

@@ -272,9 +272,12 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
       return;
     }
   }
+  // The tile list is written before the launch and only read here: read through the
+  // constant address space, it takes scalar loads (a plain load is a vector load, whose wait
+  // would also wait for the tile DMA just issued).
   auto tile_at = [&](int t) __attribute__((always_inline)) {
     if constexpr (LIST)
-      return tlist[t];
+      return ((const __attribute__((address_space(4))) int32_t*)tlist)[t];
     else if constexpr (ITEMS)
       return t0 + t;
     else
