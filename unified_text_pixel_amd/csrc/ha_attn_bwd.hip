@@ -26,8 +26,8 @@
 //   dQ^T += K^T dZ^T (A = K^T gathered from LDS by ds_read_b64_tr_b16).
 // bwd_delta: delta = rowsum(dO * O) in fp32.
 //
-// LDS tiles are row-major with 16-byte chunks XOR-swizzled by (row mod chunks per row);
-// a step tile of q' or dO keeps the G heads of one row side by side.
+// LDS tiles are row-major with 16-byte chunks XOR-swizzled by swz(row) (below); a step
+// tile of q' or dO keeps the G heads of one row side by side.
 #include <type_traits>
 
 #include "ha_internal.h"
@@ -55,12 +55,24 @@ __device__ inline float bpermute(int src_lane, float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src_lane, __builtin_bit_cast(int, x)));
 }
 
+// Chunk swizzle of tile row r: physical chunk = logical chunk ^ swz(r). The tiles are read
+// two ways. A row read has 16 lanes on 16 consecutive rows at one logical chunk, so swz must
+// be a bijection on r mod 16. A transposing read (ds_read_b64_tr_b16) has 32 lanes on 4
+// consecutive rows (4a .. 4a + 3) x 4 logical chunks (4m .. 4m + 3). With d = 128 (16
+// chunks, 256 bytes: every bank once) swz(r) = (r mod 16) ^ 4 (r mod 4) sends row 4a + i to
+// chunks 4(m ^ a ^ i) + (c ^ i), 16 distinct, where r mod 16 alone gives 4 chunks
+// (a 4-way bank conflict). d = 64 keeps r mod 8.
+template <int CPR>
+__device__ inline int swz(int row) {
+  return (row & (CPR - 1)) ^ (CPR == 16 ? (row & 3) << 2 : 0);
+}
+
 // Copies rows [row0, row0 + rows) of a row-major global tensor (row stride gstride bytes,
 // rows clamped to [0, rmax]) into LDS, ROWB bytes per row made of segments of D elements
 // (one per head), each swizzled by the row within the tile. 1 KB per DMA instruction:
 // lane L writes bytes 16L of it, i.e. row RPI*ins + L*16/ROWB of the tile, segment
-// (L*16 % ROWB) / 2D, physical chunk L % CPR, which holds logical chunk (L % CPR) ^ (row
-// mod CPR). Instruction ins is issued by wave ins mod 8; the lane's part of the address is
+// (L*16 % ROWB) / 2D, physical chunk L % CPR, which holds logical chunk (L % CPR) ^
+// swz(row). Instruction ins is issued by wave ins mod 8; the lane's part of the address is
 // computed once.
 template <int D, int ROWB, int NINS>
 struct RowDma {
@@ -82,7 +94,7 @@ struct RowDma {
       if (NINS % 8 != 0 && ins >= NINS) continue;
       const int row = ins * RPI + rho;
       const int r = min(max(row0 + row, 0), rmax);
-      const char* src = gbase + r * gstride + segb + ((pc ^ (row & (CPR - 1))) * 16);
+      const char* src = gbase + r * gstride + segb + ((pc ^ swz<CPR>(row)) * 16);
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + ins * 1024), 16, 0, 0);
     }
   }
@@ -252,7 +264,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   };
 
   // A/B operand reads of rows (q' or dO row ln, or K/V row 32 ksl + ln): chunk 2kk + hi of
-  // the row sits at (2kk) ^ kx, kx = hi ^ (ln mod CPR). Transposing reads: lane t of
+  // the row sits at (2kk) ^ kx, kx = hi ^ swz(ln). Transposing reads: lane t of
   // 16-lane group G16 points at row 16KS + 8rr + 4(G16 >> 1) + t/4 and dims 32mt + 16(G16 & 1)
   // + 4(t & 3).
 
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
     int lo = lane;
     __asm__ volatile("" : "+v"(lo));
     const int lnx = lo & 31, hix = lo >> 5;
-    const int kxx = hix ^ (lnx & (C::CPR - 1));
+    const int kxx = hix ^ swz<C::CPR>(lnx);
     // S' and dP': rows x keys, lane = key, register r = row 8(r/4) + 4hi + r%4
     f32x16 sacc = mfma(split_col(lr * kLog2e), ones, f32x16{});
     f32x16 pacc = mfma(split_col(dr), ones, f32x16{});
@@ -323,8 +335,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
       const int rl = 16 * KS + vrx, ru = rl + 8;
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) {
-        const int cl = (((4 * mt + vclx) ^ (rl & (C::CPR - 1))) * 16) + vhx;
-        const int cu = (((4 * mt + vclx) ^ (ru & (C::CPR - 1))) * 16) + vhx;
+        const int cl = (((4 * mt + vclx) ^ swz<C::CPR>(rl)) * 16) + vhx;
+        const int cu = (((4 * mt + vclx) ^ swz<C::CPR>(ru)) * 16) + vhx;
         const char* ol = oc + (rl * G + hg) * (2 * D) + cl;
         const char* ou = oc + (ru * G + hg) * (2 * D) + cu;
         const bf16x4 dol = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ol);
@@ -508,7 +520,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
     int lo = lane;
     __asm__ volatile("" : "+v"(lo));
     const int lnx = lo & 31, hix = lo >> 5;
-    const int kxx = hix ^ (lnx & (C::CPR - 1));
+    const int kxx = hix ^ swz<C::CPR>(lnx);
     // per 32-key half: S^T = K Q'^T and dP^T = V dO^T (keys x rows, lane = row), then
     // dZ^T = P^T (dP^T - delta) on allowed keys, to bf16 in B-operand order (keys
     // 16KS .. 16KS + 15 of the tile in register order)
@@ -553,8 +565,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
       const int rl = 16 * KS + vrow, ru = rl + 8;
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) {
-        const char* pl = kc + rl * (2 * D) + (((4 * mt + vclow) ^ (rl & (C::CPR - 1))) * 16) + vhalf;
-        const char* pu = kc + ru * (2 * D) + (((4 * mt + vclow) ^ (ru & (C::CPR - 1))) * 16) + vhalf;
+        const char* pl = kc + rl * (2 * D) + (((4 * mt + vclow) ^ swz<C::CPR>(rl)) * 16) + vhalf;
+        const char* pu = kc + ru * (2 * D) + (((4 * mt + vclow) ^ swz<C::CPR>(ru)) * 16) + vhalf;
         const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pl);
         const bf16x4 up4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pu);
         dq[mt] = mfma(__builtin_shufflevector(lo4, up4, 0, 1, 2, 3, 4, 5, 6, 7), zf[KS], dq[mt]);
