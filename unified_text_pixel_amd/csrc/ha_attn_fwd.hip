@@ -529,17 +529,39 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     if (i >= a.row_begin && hi == 0)
       a.lse[((int64_t)b * a.Hq + h) * S + i] = (mref + __builtin_amdgcn_logf(l)) * 0.693147180559945309f;
   }
-  if (i >= a.row_begin) {  // also excludes rows before the sequence (row_begin >= 0)
+  // The output rows go through LDS (the K/V buffers, free once every wave is past its last
+  // tile), so that the global stores write whole 2D-byte rows: stored from the MFMA layout,
+  // one row per lane, every store instruction would touch a cache line per lane. Wave w
+  // stages its 32 rows in half of buffer w / 2, 16-byte chunks XOR-swizzled by the row.
+  {
+    constexpr int CPR = TL::CPR;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    char* stg = (wave >> 1) == 0 ? k0 : ((wave >> 1) == 1 ? k1 : ((wave >> 1) == 2 ? v0 : v1));
+    stg += (wave & 1) * 32 * (2 * D);
     const float inv = 1.f / l;
-    __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * S + i) * a.Hq + h) * D;
+    const int rw = lane & 31;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x4 w = {static_cast<__bf16>(o[mt][4 * j] * inv), static_cast<__bf16>(o[mt][4 * j + 1] * inv),
                           static_cast<__bf16>(o[mt][4 * j + 2] * inv), static_cast<__bf16>(o[mt][4 * j + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(orow + 32 * mt + 8 * j + 4 * hi) = w;
+        const int chunk = (4 * mt + j) ^ (rw & (CPR - 1));  // dims 32mt + 8j .. +7
+        *reinterpret_cast<bf16x4*>(stg + rw * (2 * D) + chunk * 16 + 8 * hi) = w;
       }
+    // lane L stores chunk L mod CPR of row 64/CPR k + L / CPR
+    constexpr int RPI = 64 / CPR;
+    const int lr = lane / CPR, lc = lane % CPR;
+    const int row0 = S - (a.nq - qb) * C::BQ + tsub * 32;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int r = RPI * k + lr;
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(stg + r * (2 * D) + ((lc ^ (r & (CPR - 1))) * 16));
+      if (row0 + r >= a.row_begin)  // also excludes rows before the sequence (row_begin >= 0)
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.out) + (((int64_t)b * S + row0 + r) * a.Hq + h) * D +
+                                   8 * lc) = v8;
+    }
   }
 }
 
