@@ -88,14 +88,17 @@ struct RowDma {
 
   __device__ __attribute__((always_inline)) inline void issue(const char* gbase, int64_t gstride, int row0,
                                                                 int rmax, char* lds, int wave) const {
+    const char* tbase = gbase + (int64_t)row0 * gstride;
 #pragma unroll
     for (int j = 0; j < (NINS + 7) / 8; ++j) {
       const int ins = wave + 8 * j;  // run-time: keeps the LDS address out of constant folding
       if (NINS % 8 != 0 && ins >= NINS) continue;
       const int row = ins * RPI + rho;
       const int r = min(max(row0 + row, 0), rmax);
-      const char* src = gbase + r * gstride + segb + ((pc ^ swz<CPR>(row)) * 16);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + ins * 1024), 16, 0, 0);
+      // a uniform tile base plus a 32-bit lane offset (r >= row0 for row0 <= rmax, and the
+      // offset spans a tile), which the DMA takes as an SGPR base and one VGPR
+      const unsigned off = (unsigned)((r - row0) * (int)gstride) + segb + ((pc ^ swz<CPR>(row)) * 16);
+      __builtin_amdgcn_global_load_lds(tbase + off, (lds_void*)(lds + ins * 1024), 16, 0, 0);
     }
   }
 };
