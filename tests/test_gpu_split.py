@@ -164,3 +164,26 @@ def test_split_with_short_workspace_runs_unsplit():
         B.ha_attn_fwd(desc, pro, dev["q"], dev["k"], dev["v"], out, ws)
         torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_planner_pads_per_batch_lists():
+    """Two batch items with different layouts on 4 KV heads: XCDs 0-3 serve item 0 and 4-7
+    item 1, their sorted lists differ, so the table pads the shorter ones with empty entries.
+    For 96 CUs: 176 entries, 24 of them padding, 12 split blocks (see the split planner's
+    host tests for the sizes). Output and lse against the oracle and the unsplit run."""
+    w = small([W.Segment(C, 100), W.Segment(F, 900, (30, 30))], hq=16, hkv=4, batch=2)
+    x = W.generate(w)
+    seg = W.segment_table(w)
+    seg[1] = [[0, 700, C], [700, 300, G]]
+    x.segments = seg
+    dev = to_device(x)
+    with env(HA_SPLIT_PARTS=1):
+        ref, ref_lse, n0 = fwd_lse(x, dev)
+    with env(HA_CU_COUNT=96):
+        out, lse, n1 = fwd_lse(x, dev)
+    assert n1 > n0, "the split plan was not taken"
+    compare(f64(out), oracle.hot_path(x), "bf16", "per-batch layouts, padded item table")
+    close_to_unsplit(out, ref, "per-batch layouts")
+    err = float(np.abs(f64(lse) - oracle.path_lse(x)).max())
+    assert err <= LSE_ABS, err
+    assert float((lse - ref_lse).abs().max()) <= 1e-4

@@ -98,3 +98,14 @@ def test_forced_parts():
 def test_fp32_never_split():
     d = U.AttnDesc(1, 80, 4, 1, 64, "f32", np.array([[[0, 16, 0], [16, 64, 1]]], np.int32))
     assert nbytes(d, HA_SPLIT_PARTS=4, HA_CU_COUNT=8) == nbytes(d, HA_SPLIT_PARTS=1)
+
+
+def test_per_batch_layouts_pad_the_table():
+    """Item 0 ([100 causal][900 full]) and item 1 ([700 causal][300 image]) on 4 KV heads:
+    each XCD plans one (item, KV head) pair, so the two items' lists differ in length (item
+    0's heavy full-row blocks are split, item 1's causal blocks are not) and the table pads
+    them to the longest: 22 entries per XCD, 176 in all, 12 split blocks, 36 slots."""
+    seg = np.array([[[0, 100, 0], [100, 900, 1]], [[0, 700, 0], [700, 300, 2]]], np.int32)
+    d = U.AttnDesc(2, 1000, 16, 4, 128, "bf16", seg)
+    base = nbytes(d, HA_SPLIT_PARTS=1)
+    assert nbytes(d, HA_CU_COUNT=96) - base == plan_bytes(d, 176, 12, 36)
