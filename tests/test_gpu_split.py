@@ -90,6 +90,23 @@ def test_forced_split_small(name, parts):
         assert float((lse - ref_lse).abs().max()) <= 1e-4
 
 
+@pytest.mark.parametrize("name", ["hd_small", "gen_small", "one_token"])
+def test_forced_split_most_parts(name):
+    """64 parts, the most HA_SPLIT_PARTS takes: every block has at most 6 key tiles here, so
+    most parts are empty and each block's merge sees parts of one tile between them."""
+    w = SMALL[name]
+    x = W.generate(w)
+    dev = to_device(x)
+    with env(HA_SPLIT_PARTS=1):
+        ref, _, n0 = fwd_lse(x, dev)
+    with env(HA_SPLIT_PARTS=64):
+        out, lse, n1 = fwd_lse(x, dev)
+    assert n1 > n0
+    compare(f64(out), oracle.hot_path(x), "bf16", f"{name} in 64 parts")
+    close_to_unsplit(out, ref, name)
+    assert float(np.abs(f64(lse) - oracle.path_lse(x)).max()) <= LSE_ABS
+
+
 @pytest.mark.parametrize("alpha,sign", [(26.0, 1.0), (36.0, -1.0)])
 def test_forced_split_careful_pass(alpha, sign):
     """Scores shifted by +86 or -165 log2 units: the parts take the careful re-referencing
