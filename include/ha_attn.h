@@ -174,7 +174,8 @@ size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc*
  * rounded to the input dtype for the second product. Layouts with HA_SEG_GEN segments
  * need more of the plan than row_limit and ranges: they return HA_ERR_UNSUPPORTED here
  * (and in ha_attn_fwd_planned_from); ha_attn_fwd, ha_attn_fwd_lse and ha_attn_bwd take
- * them. */
+ * them. One work item per query block: the split plan of ha_attn_fwd (below) needs its
+ * workspace. */
 ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const void* k,
                               const void* v, const int32_t* row_limit, const int32_t* ranges,
                               void* out, void* stream);
