@@ -199,6 +199,22 @@ def test_backward_multigen_one_group():
     check("multigen dv", got["dv"][0, :, 5], want["dv"][0, :, 5])
 
 
+def test_backward_hunyuan_one_group():
+    """The HunyuanImage interleave at full size with plain image segments (S = 6016). Its
+    forward takes the split plan on 256 CUs (2 query blocks per KV head in 4 parts), so the
+    lse the backward uses comes from the merge kernel; the oracle computes KV group 2."""
+    w = W.get_config("hunyuan")
+    print("case hunyuan: group 2", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w, seed=81)
+    got = run_train(x, dout)
+    want = oracle.path_backward(x, dout, groups=[2])
+    heads = slice(8, 12)
+    check("hunyuan dq", got["dq"][0, :, heads], want["dq"][0, :, heads])
+    check("hunyuan dk", got["dk"][0, :, 2], want["dk"][0, :, 2])
+    check("hunyuan dv", got["dv"][0, :, 2], want["dv"][0, :, 2])
+
+
 def test_autograd_matches_direct_calls():
     """api.hybrid_attention_train under torch autograd gives exactly what the direct calls
     give (same kernels), including the norm-weight gradients."""
