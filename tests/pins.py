@@ -533,3 +533,66 @@ def pin_backward_invariants():
     lse = oracle.backward.attention_lse(q0, k, [M])
     counts = np.array([(i + 1) if (i < 5 or i >= 26) else (17 if i < 17 else S) for i in range(S)])
     assert np.allclose(lse[0, 0], np.log(counts), atol=1e-12)
+
+
+# ---------------------------------------------------------------- sampled rows and KV groups
+def _rows_layouts():
+    """Small layouts covering every segment kind, every rotary kind, norm on and off,
+    groups of 1, 4 and 8 query heads per KV head, two batch items."""
+    return [
+        small_workload([W.Segment(C, 9), W.Segment(F, 16, (4, 4)), W.Segment(C, 6)], hq=4, hkv=1,
+                       d=16, rope="mrope", sections=(4, 2, 2), norm=True, batch=2, seed=31),
+        small_workload([W.Segment(C, 5), W.Segment(G, 9, (3, 3)), W.Segment(C, 4),
+                        W.Segment(G, 16, (4, 4)), W.Segment(C, 3)], hq=8, hkv=1, d=16, rope="2d",
+                       norm=False, batch=2, seed=32),
+        small_workload([W.Segment(C, 4), W.Segment(GEN, 9, (3, 3)), W.Segment(C, 3),
+                        W.Segment(GEN, 4, (2, 2)), W.Segment(F, 4, (2, 2)), W.Segment(C, 2)],
+                       hq=4, hkv=4, d=8, rope="1d", norm=True, batch=2, seed=33),
+        small_workload([W.Segment(G, 6, (2, 3)), W.Segment(C, 7), W.Segment(F, 9, (3, 3))], hq=8,
+                       hkv=2, d=16, rope="none", norm=True, batch=2, seed=34),
+    ]
+
+
+def pin_rows_match_whole_path():
+    """hot_path_rows (the checker of every full-size GPU test) equals the whole-path oracle,
+    pinned on its own by the pins above, on sampled rows and heads of each batch item:
+    both run the same norm, rotary and softmax, one on a subset of rows and heads."""
+    rng = np.random.default_rng(35)
+    for w in _rows_layouts():
+        x = W.generate(w)
+        whole = oracle.pipeline.hot_path(x)
+        S, Hq = w.seq_len, w.n_q_heads
+        for b in range(w.batch):
+            for trial in range(3):
+                n = int(rng.integers(1, S))
+                rows = rng.choice(S, size=n, replace=False)
+                if trial == 0:
+                    rows = np.concatenate([[S - 1, 0], rows[:max(0, n - 2)]])
+                heads = rng.choice(Hq, size=int(rng.integers(1, Hq + 1)), replace=False)
+                got = oracle.pipeline.hot_path_rows(x, b, rows, list(heads))
+                want = whole[b][rows][:, heads]
+                assert got.shape == want.shape, (w.name, b)
+                assert np.abs(got - want).max() <= 1e-12, (b, rows.tolist(), heads.tolist())
+
+
+def pin_backward_groups_match_whole():
+    """path_backward restricted to some KV groups (the checker of the full-size backward
+    GPU tests) equals the entries of the whole call, pinned by finite differences and torch
+    autograd above, for those groups: dq of the group's query heads, dk and dv of the
+    group; and it leaves every other entry unset."""
+    import oracle.backward
+    rng = np.random.default_rng(36)
+    for w in _rows_layouts():
+        x = W.generate(w)
+        dout = rng.standard_normal((w.batch, w.seq_len, w.n_q_heads, w.head_dim))
+        whole = oracle.backward.path_backward(x, dout)
+        grp = w.n_q_heads // w.n_kv_heads
+        for g in range(w.n_kv_heads):
+            part = oracle.backward.path_backward(x, dout, groups=[g])
+            hs = slice(g * grp, (g + 1) * grp)
+            assert np.abs(part["dq"][:, :, hs] - whole["dq"][:, :, hs]).max() <= 1e-12, (w.name, g)
+            assert np.abs(part["dk"][:, :, g] - whole["dk"][:, :, g]).max() <= 1e-12, (w.name, g)
+            assert np.abs(part["dv"][:, :, g] - whole["dv"][:, :, g]).max() <= 1e-12, (w.name, g)
+            others = [h for h in range(w.n_q_heads) if h // grp != g]
+            assert np.isnan(part["dq"][:, :, others]).all(), (w.name, g)
+            assert np.isnan(np.delete(part["dk"], g, axis=2)).all(), (w.name, g)

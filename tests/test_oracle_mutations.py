@@ -255,6 +255,68 @@ MUTATIONS.update({
 })
 
 
+# ---- sampled rows and KV-group subsets (the checkers of the full-size GPU tests)
+def _rows_positions_by_item(inputs, b, rows, heads, dtype=np.float64):
+    """hot_path_rows with the positions cut to the batch item but not to the sampled rows
+    (the first len(rows) tokens' positions rotate the sampled q rows)."""
+    w = inputs.workload
+    rows = np.asarray(rows, dtype=np.int64)
+    q = np.asarray(inputs.q[b:b + 1, rows], dtype=dtype)
+    k = np.asarray(inputs.k[b:b + 1], dtype=dtype)
+    if w.qk_norm:
+        q = oracle.norm.rms_norm(q, inputs.w_q, w.norm_eps, dtype=dtype)
+        k = oracle.norm.rms_norm(k, inputs.w_k, w.norm_eps, dtype=dtype)
+    q = oracle.pipeline._rotary(q, w, inputs.positions[b:b + 1, :len(rows)], dtype)[0]
+    k = oracle.pipeline._rotary(k, w, inputs.positions[b:b + 1], dtype)[0]
+    mrows = oracle.mask.mask_rows(inputs.segments[b], w.seq_len, rows)
+    return oracle.masked_attention.attention_rows(q, k, inputs.v[b], mrows, np.arange(len(rows)),
+                                                  heads, dtype=dtype)
+
+
+def _attention_rows_modulo_group(q, k, v, mask_rows, rows, heads, scale=None, dtype=np.float64):
+    """attention_rows with KV head h mod Hkv instead of h div (Hq / Hkv)."""
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    scale = (1.0 / np.sqrt(d)) if scale is None else scale
+    rows = np.asarray(rows)
+    out = np.empty((len(rows), len(heads), d), dtype=dtype)
+    for hi, h in enumerate(heads):
+        g = h % Hkv
+        Z = np.where(mask_rows, (q[rows, h, :] @ k[:, g, :].T) * scale, -np.inf)
+        P = np.exp(Z - Z.max(-1, keepdims=True))
+        out[:, hi, :] = (P / P.sum(-1, keepdims=True)) @ v[:, g, :]
+    return out
+
+
+_orig_attention_backward = oracle.backward.attention_backward
+
+
+def _bwd_groups_enumerated(q, k, v, masks, dout, scale=None, groups=None):
+    """attention_backward that takes the K and V of the i-th requested group from KV head i
+    (right for a whole call, where the i-th group is group i; wrong for a subset)."""
+    if groups is None:
+        return _orig_attention_backward(q, k, v, masks, dout, scale=scale)
+    Hkv = k.shape[2]
+    order = list(groups)
+    perm = list(range(Hkv))
+    for i, g in enumerate(order):
+        perm[g] = i
+    kk = np.asarray(k)[:, :, perm]
+    vv = np.asarray(v)[:, :, perm]
+    return _orig_attention_backward(q, kk, vv, masks, dout, scale=scale, groups=groups)
+
+
+MUTATIONS.update({
+    "rows_positions_by_item_only": ([(oracle.pipeline, "hot_path_rows", _rows_positions_by_item)],
+                                    ["pin_rows_match_whole_path"]),
+    "rows_head_to_group_modulo": ([(oracle.masked_attention, "attention_rows", _attention_rows_modulo_group),
+                                   (oracle.pipeline, "attention_rows", _attention_rows_modulo_group)],
+                                  ["pin_rows_match_whole_path"]),
+    "bwd_groups_enumerated_kv": ([(oracle.backward, "attention_backward", _bwd_groups_enumerated)],
+                                 ["pin_backward_groups_match_whole"]),
+})
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     patches, pin_names = MUTATIONS[name]
