@@ -29,8 +29,22 @@ The training backward (ha_attn_bwd after ha_attn_fwd_lse) is timed on its own af
 and reported under "backward" (8 d FLOP per allowed pair and query head); it is not part
 of the step.
 
+"configs" times every other workload shape: the whole ha_attn_fwd call (classifier, split
+plan, prologue, attention, merge) and, where the planned path takes the layout, the
+attention kernel alone (ha_attn_fwd_planned), each call between HIP events.
+
+"clocks" samples the GPU's core (sclk) and memory (mclk) clocks through amdsmi from a
+thread while the step runs back to back for about a second ("clock_window"), and reports
+the attention kernel's fraction of the bf16 peak at the measured core clock beside the
+fraction of the published peak (which assumes 2.4 GHz).
+
+"careful_pass" times the attention at the HunyuanImage layout when one KV group's scores
+are shifted by about +86 log2 units (which sends its work items through the careful
+re-referencing pass) against the same inputs unshifted.
+
     python bench.py [--steps K] [--warmup W] [--workload hd2048] [--no-cpu-baseline] [--no-backward]
-                    [--no-prefix] [--no-training-layouts] [--no-qkv]
+                    [--no-prefix] [--no-training-layouts] [--no-qkv] [--no-configs] [--no-clocks]
+                    [--no-careful]
 """
 from __future__ import annotations
 
@@ -88,9 +102,11 @@ def cpu_baseline(w, x, target_s=12.0):
     (their query heads) of batch item 0, then item 1, ..., until about target_s seconds are
     spent or the whole workload is done."""
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     import workloads as W
 
+    n_threads = os.cpu_count() or 1
+    limiter = threadpool_limits(limits=n_threads, user_api="blas")  # every host core, stated
     group = w.n_q_heads // w.n_kv_heads
     flops, elapsed, done = 0.0, 0.0, []
     for b in range(w.batch):
@@ -111,15 +127,16 @@ def cpu_baseline(w, x, target_s=12.0):
             heads += group
         if heads < w.n_q_heads:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
+    limiter.restore_original_limits()
     per_item = {}
     for b, h in done:
         per_item[b] = per_item.get(b, 0) + group
     what = ", ".join(f"item {b}: {n} of {w.n_q_heads} query heads" for b, n in per_item.items())
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "blas_threads_set": n_threads,
             "sample": f"{what}; whole path per head group (norm, mRoPE, explicit mask, fp64 "
-                      f"attention), {elapsed:.1f} s; host os.cpu_count()={os.cpu_count()}"}
+                      f"attention), {elapsed:.1f} s; BLAS threads set to os.cpu_count()={n_threads}"}
 
 
 def prefix_leg(w, x, sets, desc, pro, stream, step, warmup, steps):
@@ -327,6 +344,238 @@ def backward_leg(w, x, dev, useful_fwd, stream, warmup, steps, nsets):
             "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "calls": n}
 
 
+class ClockSampler:
+    """Polls the GPU's current core and memory clocks (MHz) through amdsmi from a thread, about
+    every millisecond, between start() and stop(). Records why when amdsmi is unavailable."""
+
+    def __init__(self, interval_s=0.001):
+        import threading
+        self.interval = interval_s
+        self.sclk, self.mclk, self.error = [], [], None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception as e:  # noqa: BLE001  (no SMI access: the record says so)
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        smi = self._smi
+        g = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)
+        m = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.MEM)
+        return float(g["clk"]), float(m["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                g, m = self._read()
+                self.sclk.append(g)
+                self.mclk.append(m)
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            time.sleep(self.interval)
+
+    def start(self):
+        import threading
+        if self.error is None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        def st(v):
+            if not v:
+                return None
+            a = np.array(v)
+            return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()), "samples": len(v)}
+        return {"source": "amdsmi_get_clock_info (current clock, MHz)", "sclk_mhz": st(self.sclk),
+                "mclk_mhz": st(self.mclk), "error": self.error}
+
+
+def clock_window(step, sets, stream, useful, seconds=1.0):
+    """The step back to back for about `seconds` with the clock sampler running; HIP events
+    around every attention launch. Returns the clocks and the attention throughput of that
+    window, with its fraction of the bf16 peak at the measured core clock."""
+    import torch
+    sampler = ClockSampler()
+    probe = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step(sets[0], probe)
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-4)
+    n = int(min(5000, max(50, seconds / per)))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    sampler.start()
+    for i in range(n):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    sampler.stop()
+    att = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    tf = useful / (float(att.mean()) / 1e3) / 1e12
+    out = sampler.summary()
+    out.update({"steps": n, "attn_kernel_ms": {"mean": float(att.mean()), "median": float(np.median(att))},
+                "attn_tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS})
+    if out["sclk_mhz"]:
+        peak = 256 * 4096 * out["sclk_mhz"]["median"] * 1e6 / 1e12
+        out["bf16_peak_at_measured_sclk_tflops"] = peak
+        out["frac_at_measured_sclk"] = tf / peak
+    return out
+
+
+def _timed_calls(fn, stream, n):
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, e in enumerate(ev):
+        e[0].record(stream)
+        fn(i)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+
+def configs_leg(names, warmup, steps):
+    """Every workload shape besides the headline: the whole ha_attn_fwd call (classifier,
+    split plan where the planner takes one, prologue, attention, merge) and, for layouts the
+    planned path takes (no Gen Images), the attention kernel alone (ha_attn_fwd_planned after
+    one classifier and prologue call). HIP events around each call on the launch stream;
+    input sets cycled so that together they exceed the 256 MB Infinity Cache."""
+    import torch
+    import workloads as W
+    from unified_text_pixel_amd import api, binding as B
+    from workloads.device import to_device
+    stream = torch.cuda.current_stream()
+    all_cfg = dict(W.CONFIGS)
+    all_cfg.update(W.page_shape_configs())
+    res = {}
+    for name in names:
+        w = all_cfg[name]
+        x = W.generate(w)
+        dev = to_device(x)
+        desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments)
+        pdesc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments,
+                           q_prescaled=1)
+        cs = api.rope_table(w.rope_theta, w.head_dim, w.seq_len) if w.rope != "none" else None
+        pro = B.PrologueDesc(w.rope, dev["positions"], cs, 0 if cs is None else cs.shape[0],
+                             dev["w_q"], dev["w_k"], w.norm_eps, w.mrope_sections)
+        ppro = B.PrologueDesc(w.rope, dev["positions"], cs, 0 if cs is None else cs.shape[0],
+                              dev["w_q"], dev["w_k"], w.norm_eps, w.mrope_sections,
+                              q_out_scale=B.ha_q_prescale(pdesc))
+        nbytes = B.ha_attn_workspace_bytes(desc, pro)
+        set_bytes = 3 * dev["q"].numel() * dev["q"].element_size() + 3 * dev["k"].numel() * dev["k"].element_size()
+        nsets = int(min(6, max(1, -(-300e6 // set_bytes))))
+        _, _, nq, _ = B.ha_tile_shape(desc)
+        sets = []
+        for _ in range(nsets):
+            sets.append({"q": dev["q"].clone(), "k": dev["k"].clone(), "v": dev["v"].clone(),
+                         "out": torch.empty_like(dev["q"]), "qr": torch.empty_like(dev["q"]),
+                         "kr": torch.empty_like(dev["k"]),
+                         "ws": torch.empty(max(256, nbytes), dtype=torch.uint8, device="cuda"),
+                         "ranges": torch.empty((w.batch, nq, 2), dtype=torch.int32, device="cuda"),
+                         "lim": torch.empty((w.batch, w.seq_len), dtype=torch.int32, device="cuda")})
+        pairs = sum(allowed_pairs(x.segments[b], w.seq_len) for b in range(w.batch))
+        useful = 4.0 * w.head_dim * w.n_q_heads * pairs
+
+        def whole(i):
+            s = sets[i % nsets]
+            B.ha_attn_fwd(desc, pro, s["q"], s["k"], s["v"], s["out"], s["ws"], stream=stream)
+
+        for i in range(max(2, warmup)):
+            whole(i)
+        n = max(10, steps // 2)
+        ms = _timed_calls(whole, stream, n)
+        r = {"description": w.description, "batch": w.batch, "seq_len": w.seq_len,
+             "allowed_pairs": pairs, "useful_gflop": useful / 1e9, "sets": nsets,
+             "fwd_ms": {"mean": float(ms.mean()), "median": float(np.median(ms))},
+             "fwd_tflops": useful / (float(np.median(ms)) / 1e3) / 1e12,
+             "split_plan": nbytes > B.ha_attn_workspace_bytes(
+                 B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments,
+                            split_parts=1), pro)}
+        if not any(int(k) == 3 for k in x.segments[..., 2].ravel()):
+            for s in sets:
+                B.ha_classify_tiles(pdesc, None, s["ranges"], s["lim"], stream)
+                B.ha_qk_prologue(pdesc, ppro, s["q"], s["k"], s["qr"], s["kr"], stream)
+
+            def planned(i):
+                s = sets[i % nsets]
+                B.ha_attn_fwd_planned(pdesc, s["qr"], s["kr"], s["v"], s["lim"], s["ranges"], s["out"], stream)
+
+            for i in range(max(2, warmup)):
+                planned(i)
+            am = _timed_calls(planned, stream, n)
+            tf = useful / (float(am.mean()) / 1e3) / 1e12
+            r.update({"attn_kernel_ms": {"mean": float(am.mean()), "median": float(np.median(am)),
+                                         "p10": float(np.percentile(am, 10)), "p90": float(np.percentile(am, 90))},
+                      "attn_tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS})
+        res[name] = r
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
+def careful_leg(warmup, steps, shift=26.0, group=3):
+    """The HunyuanImage layout with no rotation (so a shift is the same for every key of a
+    row) and q/k unnormalised, as it is: clean inputs against inputs where query component 0
+    of KV group `group`'s query heads and key component 0 of that group from key 300 on are
+    raised by `shift`, which moves those rows' scores by about shift^2 * scale * log2(e) =
+    +86 log2 units and sends the group's work items through the careful re-referencing pass.
+    With the XCD-aware order that group's items all run on one XCD, so the kernel time is
+    that XCD's time: the ratio of the two kernel times is about the careful pass's cost per
+    affected work item."""
+    import torch
+    import workloads as W
+    from unified_text_pixel_amd import binding as B
+    from workloads.device import to_device
+    stream = torch.cuda.current_stream()
+    w = W.get_config("hunyuan").replace(rope="none")
+    res = {"layout": "hunyuan segments, no rotation", "shift_log2": shift * shift / np.sqrt(w.head_dim) * np.log2(np.e),
+           "kv_group": group}
+    G = w.n_q_heads // w.n_kv_heads
+    for label in ("clean", "shifted"):
+        x = W.generate(w)
+        if label == "shifted":
+            x.q[:, :, group * G:(group + 1) * G, 0] += shift
+            x.k[:, 300:, group, 0] += shift
+            bits = W.f32_to_bf16_bits(x.q)
+            x.q, x.q_bits = W.bf16_bits_to_f32(bits).reshape(x.q.shape), bits.reshape(x.q.shape)
+            bits = W.f32_to_bf16_bits(x.k)
+            x.k, x.k_bits = W.bf16_bits_to_f32(bits).reshape(x.k.shape), bits.reshape(x.k.shape)
+        dev = to_device(x)
+        desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments)
+        _, _, nq, _ = B.ha_tile_shape(desc)
+        ranges = torch.empty((w.batch, nq, 2), dtype=torch.int32, device="cuda")
+        lim = torch.empty((w.batch, w.seq_len), dtype=torch.int32, device="cuda")
+        B.ha_classify_tiles(desc, None, ranges, lim, stream)
+        out = torch.empty_like(dev["q"])
+        ws = torch.empty(max(256, B.ha_attn_workspace_bytes(desc, None)), dtype=torch.uint8, device="cuda")
+
+        def planned(i):
+            B.ha_attn_fwd_planned(desc, dev["q"], dev["k"], dev["v"], lim, ranges, out, stream)
+
+        def whole(i):
+            B.ha_attn_fwd(desc, None, dev["q"], dev["k"], dev["v"], out, ws, stream=stream)
+
+        for i in range(max(2, warmup)):
+            planned(i)
+            whole(i)
+        n = max(10, steps // 2)
+        am, wm = _timed_calls(planned, stream, n), _timed_calls(whole, stream, n)
+        res[label] = {"attn_kernel_ms": float(np.median(am)), "fwd_ms": float(np.median(wm))}
+    res["kernel_ratio"] = res["shifted"]["attn_kernel_ms"] / res["clean"]["attn_kernel_ms"]
+    res["fwd_ratio"] = res["shifted"]["fwd_ms"] / res["clean"]["fwd_ms"]
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +588,9 @@ def main():
     ap.add_argument("--no-prefix", action="store_true")
     ap.add_argument("--no-training-layouts", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true")
+    ap.add_argument("--no-careful", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -452,6 +704,8 @@ def main():
                               "unit": "GB/s", "frac": pro_gbps / HBM_PEAK_GBPS},
         "attn_kernel_sha": kernel_sha(),
     }
+    if not args.no_clocks:
+        rec["clocks"] = clock_window(step, sets, stream, useful)
     if not args.no_prefix:
         rec["prefix_step"] = prefix_leg(w, x, sets, desc, pro, stream, step, args.warmup, args.steps)
     if not args.no_backward and w.dtype == "bf16":
@@ -460,6 +714,13 @@ def main():
         rec["qkv_projection"] = qkv_leg(w, x, dev, stream, args.warmup, args.steps)
     if not args.no_training_layouts:
         rec["training_layouts"] = training_layout_leg(["hunyuan_multigen", "hunyuan"], args.warmup, args.steps)
+    if not args.no_configs:
+        names = [n for n in ("hd1024", "edit", "hunyuan", "hunyuan_multigen", "page1024", "page2048")
+                 if n != w.name]
+        print("bench: timing the other workload shapes", file=sys.stderr, flush=True)
+        rec["configs"] = configs_leg(names, args.warmup, args.steps)
+    if not args.no_careful:
+        rec["careful_pass"] = careful_leg(args.warmup, args.steps)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, x)

@@ -30,12 +30,16 @@
  *    through the explicit q_out == q_in / k_out == k_in alias of ha_qk_prologue.
  *  - Streams: every launch is asynchronous on the caller's hipStream_t, passed as void*
  *    (NULL = the default stream). No call synchronises, unless the environment variable
- *    HA_DEBUG=1 is set, which synchronises and checks for errors after each launch.
- *  - Errors: every argument is validated on the host before any HIP call. A bad call
- *    returns a nonzero ha_status, sets the thread's ha_last_error() text, and touches
- *    neither the device nor the stream. A failed launch returns HA_ERR_HIP with the HIP
- *    error text. No C++ exception crosses this interface. The library keeps no state
- *    between calls apart from that error text.
+ *    HA_DEBUG=1 is set (read at each call), which synchronises and checks for errors after
+ *    each launch, and checks rotary positions on the device before they are used: a
+ *    position outside [0, n_pos) then fails the call with HA_ERR_INVALID_ARG (without
+ *    HA_DEBUG such positions are clamped to that range; the pages' contract convention
+ *    is to reject contract errors, hidream-o1-p100a model card, "Serving (HTTP)").
+ *  - Errors: every argument is validated on the host before any HIP call (HA_DEBUG's
+ *    position check aside). A bad call returns a nonzero ha_status, sets the thread's
+ *    ha_last_error() text, and touches neither the device nor the stream. A failed launch
+ *    returns HA_ERR_HIP with the HIP error text. No C++ exception crosses this interface.
+ *    The library keeps no state between calls apart from that error text.
  *  - Empty work (batch == 0 or seq_len == 0) is valid and launches nothing.
  */
 #ifndef HA_ATTN_H
@@ -48,7 +52,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 4
+#define HA_ABI_VERSION 5
 #define HA_MAX_SEGMENTS 64      /* segments per batch item */
 #define HA_MAX_SEQ_LEN (1 << 22)
 
@@ -89,6 +93,11 @@ typedef struct {
   int32_t q_prescaled;      /* ha_attn_fwd_planned only: 1 when q already carries the factor
                                scale * log2(e) (ha_qk_prologue with q_out_scale set to
                                ha_q_prescale(desc)), 0 for plain q */
+  int32_t split_parts;      /* split plan of the bf16 forward (see ha_attn_fwd): 0 lets the
+                               planner decide, 1 never splits, P in [2, 64] splits every
+                               query block into P parts */
+  int32_t plan_cus;         /* CUs the planner balances the work items over: 0 means the
+                               current device's count, n > 0 plans for n CUs */
 } ha_attn_desc;
 
 /* q/k prologue: RMSNorm over head_dim (y = x / sqrt(mean(x^2) + eps) * w, before the
@@ -100,7 +109,8 @@ typedef struct {
  *                  rotation once it holds mrope_sections[axis] pairs ([B][S][3]);
  *                  [24,20,20] gives i mod 3 for i < 60 and T for 60..63
  *   HA_ROPE_NONE   no rotation (positions and cos_sin may be NULL)
- * Positions outside [0, n_pos) are clamped to that range. */
+ * Positions must lie in [0, n_pos): HA_DEBUG=1 checks them on the device and fails the call
+ * otherwise; without it, out-of-range positions are clamped to that range. */
 typedef struct {
   int32_t rope_kind;            /* ha_rope_kind */
   int32_t mrope_sections[3];    /* HA_ROPE_MROPE only; non-negative, sum head_dim / 2 */
@@ -163,8 +173,8 @@ ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
 /* Workspace bytes ha_attn_fwd needs: row limits, tile ranges, and the rotated q and k
  * when pro is not NULL; with HA_SEG_GEN segments also per-key visibility and per query
  * block tile lists; with a split plan (below) its work item table and fp32 partial
- * results. The plan depends on the current device's CU count, so call this with the
- * device current that will run the forward. */
+ * results. The plan depends on the CU count (desc->plan_cus, else the current device's),
+ * so call this with the device current that will run the forward. */
 size_t ha_attn_workspace_bytes(const ha_attn_desc* desc, const ha_prologue_desc* pro);
 
 /* Attention on prepared inputs: q and k already normalised and rotated (q optionally
@@ -187,15 +197,15 @@ ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const voi
  *
  * Split plan (bf16): where the heaviest query blocks would leave the CUs partly idle in
  * their last round (e.g. the HunyuanImage 3.0 interleave, or fewer blocks than CUs), the
- * host splits some blocks' key tiles into parts that run as separate work items and a
- * merge kernel combines them (the merge rounds differently from one work item: results
- * agree within bf16 rounding, not bit for bit, with ha_attn_fwd_planned). The work item
- * table goes to the workspace by an asynchronous copy from pinned host memory that the
- * library allocates once per distinct table (at most 256, kept until the process ends).
- * A workspace smaller than ha_attn_workspace_bytes but large enough without the plan runs
- * without it. Environment, read at each call: HA_SPLIT_PARTS=1 disables the plan,
- * HA_SPLIT_PARTS=P > 1 splits every block into P parts, HA_CU_COUNT=n plans for n CUs
- * (the last two for tests). */
+ * host decides, from the segment table, to split some blocks' key tiles into parts that
+ * run as separate work items, and a merge kernel combines them (the merge rounds
+ * differently from one work item: results agree within bf16 rounding, not bit for bit,
+ * with ha_attn_fwd_planned). A kernel builds the work item table in the workspace from
+ * the classifier's per-block tile counts (longest first on each XCD), so the call copies
+ * nothing from the host and allocates nothing. The plan covers at most 1024 work items per
+ * XCD before splitting; larger problems run one work item per query block. A workspace
+ * smaller than ha_attn_workspace_bytes but large enough without the plan runs without
+ * it. desc->split_parts and desc->plan_cus override the planner (for tests). */
 ha_status ha_attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
                       const void* k, const void* v, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
@@ -217,8 +227,10 @@ ha_status ha_qk_prologue_from(const ha_attn_desc* desc, const ha_prologue_desc* 
 
 /* ha_attn_fwd_planned for the query rows [row_begin, seq_len) only: the query blocks that
  * hold them are computed (from all of q, k, v: the prefix's q, k, v must be in place), and
- * out rows below row_begin are not written. Exact when rows below row_begin do not attend
- * to changed keys, which holds for a causal prefix. 0 <= row_begin <= seq_len. */
+ * out rows below row_begin are not written. 0 <= row_begin <= seq_len, and no row below
+ * row_begin may attend to a key at or after it (so the kept rows are exact): a full
+ * segment that starts below row_begin < seq_len, or an image segment that row_begin cuts,
+ * fails the call with HA_ERR_INVALID_ARG. A causal prefix qualifies. */
 ha_status ha_attn_fwd_planned_from(const ha_attn_desc* desc, const void* q, const void* k,
                                    const void* v, const int32_t* row_limit, const int32_t* ranges,
                                    void* out, int32_t row_begin, void* stream);

@@ -19,26 +19,26 @@ from workloads.device import to_device
 BF16_MAX, BF16_MEAN, F32_REL = 2e-2, 2e-3, 1e-5
 
 
+_PLAN = {"split_parts": 0, "plan_cus": 0}
+
+
 @contextlib.contextmanager
-def env(**kv):
-    """Set environment variables the library reads at each call (HA_SPLIT_PARTS,
-    HA_CU_COUNT) for the duration of a block."""
-    old = {k: os.environ.get(k) for k in kv}
-    os.environ.update({k: str(v) for k, v in kv.items()})
+def plan(split_parts=0, plan_cus=0):
+    """Descriptors made by desc_for inside the block carry these split-plan overrides
+    (ha_attn_desc.split_parts: 1 never splits, P > 1 splits every query block into P parts;
+    plan_cus: plan for that many CUs instead of the device's)."""
+    old = dict(_PLAN)
+    _PLAN.update(split_parts=int(split_parts), plan_cus=int(plan_cus or 0))
     try:
         yield
     finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        _PLAN.update(old)
 
 
 def unsplit():
     """The bf16 forward without split query blocks: one work item per query block, the
     summation order of ha_attn_fwd_planned."""
-    return env(HA_SPLIT_PARTS=1)
+    return plan(split_parts=1)
 
 
 def require_gpu():
@@ -49,7 +49,8 @@ def require_gpu():
 
 def desc_for(w: W.Workload, segments=None) -> B.AttnDesc:
     seg = W.segment_table(w) if segments is None else segments
-    return B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, seg)
+    return B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, seg,
+                      split_parts=_PLAN["split_parts"], plan_cus=_PLAN["plan_cus"])
 
 
 def prologue_for(w: W.Workload, dev) -> B.PrologueDesc | None:

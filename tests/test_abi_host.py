@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     assert len(names) == 16 and sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
-    assert U.ha_abi_version() == 4
+    assert U.ha_abi_version() == 5
 
 
 def seg(rows, batch=1):
@@ -59,6 +59,9 @@ BAD_DESCS = [
     (dict(batch=-1), B.HA_ERR_INVALID_ARG, ">= 0"),
     (dict(n_kv_heads=0), B.HA_ERR_INVALID_ARG, "head counts"),
     (dict(q_prescaled=2), B.HA_ERR_INVALID_ARG, "q_prescaled"),
+    (dict(split_parts=-1), B.HA_ERR_INVALID_ARG, "split_parts"),
+    (dict(split_parts=65), B.HA_ERR_INVALID_ARG, "split_parts"),
+    (dict(plan_cus=-3), B.HA_ERR_INVALID_ARG, "plan_cus"),
 ]
 
 
@@ -258,6 +261,23 @@ def test_prefix_entry_points_check_ranges():
     U.ha_attn_fwd_planned_from(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 80, stream=0)
     U.ha_qk_prologue_from(d, U.PrologueDesc("none"), FAKE, FAKE, FAKE, FAKE, 80, stream=0)
     assert U.ha_last_error() == ""
+
+
+def test_prefix_entry_point_refuses_rows_that_see_later_keys():
+    """ha_attn_fwd_planned_from keeps the rows below row_begin from an earlier step, so it
+    refuses a row_begin below which some row attends to a key at or after it: inside or
+    after the start of a full segment (its rows see every key), or inside an image segment
+    (its rows see their whole segment). The check runs on the host, before any launch."""
+    full = desc(segments=seg([[0, 16, 0], [16, 64, 1]], batch=2), batch=2)
+    gca = desc(segments=seg([[0, 16, 0], [16, 32, 2], [48, 32, 0]]))
+    for d, p in ((full, 17), (full, 40), (full, 79), (gca, 17), (gca, 47)):
+        with pytest.raises(U.HAError) as e:
+            U.ha_attn_fwd_planned_from(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, p, stream=0)
+        assert e.value.status == B.HA_ERR_INVALID_ARG and "attend to keys at or after" in str(e.value), p
+    # the same rule as the torch layer's check
+    from unified_text_pixel_amd.api import prefix_is_invariant
+    for d, p in ((full, 17), (gca, 20)):
+        assert not prefix_is_invariant(d._seg_np, d.c.seq_len, p)
 
 
 def test_gen_image_layouts():

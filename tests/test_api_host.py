@@ -16,7 +16,7 @@ def _random_table(rng, batch, S):
     for _ in range(batch):
         cuts = np.sort(rng.choice(np.arange(1, S), size=min(S - 1, int(rng.integers(0, 5))), replace=False))
         bounds = [0, *cuts.tolist(), S]
-        items.append([[a, b - a, int(rng.integers(0, 3))] for a, b in zip(bounds, bounds[1:])])
+        items.append([[a, b - a, int(rng.integers(0, 4))] for a, b in zip(bounds, bounds[1:])])
     n = max(len(it) for it in items)
     for it in items:
         it += [[S, 0, 0]] * (n - len(it))

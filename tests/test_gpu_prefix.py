@@ -88,8 +88,10 @@ def test_row_begin_zero_is_the_planned_path():
 
 
 def test_rows_before_row_begin_untouched():
-    """Rows below row_begin keep what the buffer held, even inside a computed block."""
-    w = hidream(70, 16, batch=1, seed=43)
+    """Rows below row_begin keep what the buffer held, even inside a computed block (row 100
+    of the causal text lies inside the block of rows [86, 150), the sequence being 406 long
+    with blocks of 64 aligned to its end)."""
+    w = hidream(150, 16, batch=1, seed=43)
     x = W.generate(w)
     dev = to_device(x)
     desc = B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, "bf16", x.segments)
@@ -98,13 +100,14 @@ def test_rows_before_row_begin_untouched():
     lim = torch.empty((w.batch, w.seq_len), dtype=torch.int32, device="cuda")
     B.ha_classify_tiles(desc, None, ranges, lim)
     out = torch.full_like(dev["q"], 7.0)
-    B.ha_attn_fwd_planned_from(desc, dev["q"], dev["k"], dev["v"], lim, ranges, out, 90)
+    assert (w.seq_len - 100) % bq != 0, "row 100 must sit inside a block"
+    B.ha_attn_fwd_planned_from(desc, dev["q"], dev["k"], dev["v"], lim, ranges, out, 100)
     torch.cuda.synchronize()
-    assert bool((out[:, :90] == 7.0).all())
+    assert bool((out[:, :100] == 7.0).all())
     ref = torch.empty_like(dev["q"])
     B.ha_attn_fwd_planned(desc, dev["q"], dev["k"], dev["v"], lim, ranges, ref)
     torch.cuda.synchronize()
-    assert torch.equal(out[:, 90:], ref[:, 90:])
+    assert torch.equal(out[:, 100:], ref[:, 100:])
 
 
 @pytest.mark.parametrize("rope,norm", [("mrope", True), ("none", False)])
@@ -120,6 +123,11 @@ def test_api_forward_from_over_steps(rope, norm):
                                mrope_sections=w.mrope_sections,
                                q_norm_weight=dev["w_q"] if norm else None,
                                k_norm_weight=dev["w_k"] if norm else None, eps=w.norm_eps)
+    whole = api.HybridAttention(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, "bf16",
+                                x.segments, rope=w.rope, positions=dev["positions"], theta=w.rope_theta,
+                                mrope_sections=w.mrope_sections,
+                                q_norm_weight=dev["w_q"] if norm else None,
+                                k_norm_weight=dev["w_k"] if norm else None, eps=w.norm_eps, split_parts=1)
     q, k, v = dev["q"].clone(), dev["k"].clone(), dev["v"].clone()
     gen = torch.Generator(device="cuda").manual_seed(3)
     for step in range(3):
@@ -127,8 +135,7 @@ def test_api_forward_from_over_steps(rope, norm):
             for t in (q, k, v):
                 t[:, 66:] = torch.randn(t[:, 66:].shape, generator=gen, device="cuda").to(t.dtype)
         got = attn.forward_from(q, k, v, 66 if step else 0)
-        with unsplit():
-            want = attn(q, k, v)
+        want = whole(q, k, v)
         torch.cuda.synchronize()
         assert torch.equal(got, want), f"step {step}"
     with pytest.raises(ValueError):

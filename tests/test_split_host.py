@@ -2,10 +2,8 @@
 
 ha_attn_workspace_bytes grows by the plan's work item table and fp32 partial results exactly
 when the planner splits query blocks, so the workspace size shows its decisions. The CU count
-comes from HA_CU_COUNT (without a device, and without it, nothing is split); HA_SPLIT_PARTS=1
-disables the plan and HA_SPLIT_PARTS=P splits every block into P parts."""
-import os
-
+comes from the descriptor's plan_cus (without a device, and without it, nothing is split);
+split_parts = 1 disables the plan and split_parts = P splits every block into P parts."""
 import numpy as np
 import pytest
 
@@ -23,20 +21,14 @@ def wdesc(name):
                       W.segment_table(w))
 
 
-def nbytes(d, **env):
-    keys = ("HA_CU_COUNT", "HA_SPLIT_PARTS")
-    old = {k: os.environ.get(k) for k in keys}
+def nbytes(d, split_parts=0, plan_cus=0):
+    """Workspace bytes with the descriptor's split_parts and plan_cus set as given."""
+    old = (d.c.split_parts, d.c.plan_cus)
     try:
-        for k in keys:
-            os.environ.pop(k, None)
-        os.environ.update({k: str(v) for k, v in env.items()})
+        d.c.split_parts, d.c.plan_cus = int(split_parts), int(plan_cus)
         return U.ha_attn_workspace_bytes(d)
     finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        d.c.split_parts, d.c.plan_cus = old
 
 
 def plan_bytes(d, n_items, n_splits, n_slots):
@@ -57,7 +49,7 @@ def test_no_cu_count_no_split():
         pass
     for name in ("hunyuan", "hd1024"):
         d = wdesc(name)
-        assert nbytes(d) == nbytes(d, HA_SPLIT_PARTS=1)
+        assert nbytes(d) == nbytes(d, split_parts=1)
 
 
 def test_hunyuan_on_256_cus():
@@ -66,8 +58,8 @@ def test_hunyuan_on_256_cus():
     them fill 2 rounds of 32 CUs; the other 2 are split into 4 parts each: 100 items per XCD,
     16 split blocks in all, 64 partial slots."""
     d = wdesc("hunyuan")
-    base = nbytes(d, HA_SPLIT_PARTS=1)
-    assert nbytes(d, HA_CU_COUNT=256) - base == plan_bytes(d, 800, 16, 64)
+    base = nbytes(d, split_parts=1)
+    assert nbytes(d, plan_cus=256) - base == plan_bytes(d, 800, 16, 64)
 
 
 @pytest.mark.parametrize("name,cus,split", [("hd2048", 256, False), ("edit", 256, False),
@@ -79,25 +71,25 @@ def test_planner_decisions(name, cus, split):
     hunyuan_multigen's heaviest blocks skip the first Gen Image (76 tiles) and fill 2 rounds;
     on 30 CUs per XCD they leave 4 over, which are split."""
     d = wdesc(name)
-    base = nbytes(d, HA_SPLIT_PARTS=1)
-    got = nbytes(d, HA_CU_COUNT=cus)
+    base = nbytes(d, split_parts=1)
+    got = nbytes(d, plan_cus=cus)
     assert (got > base) == split, (name, cus, got - base)
 
 
 def test_forced_parts():
-    """HA_SPLIT_PARTS=3: every (KV head, query block) in 3 parts, whatever the CU count."""
+    """split_parts = 3: every (KV head, query block) in 3 parts, whatever the CU count."""
     d = U.AttnDesc(1, 80, 8, 2, 128, "bf16", np.array([[[0, 16, 0], [16, 64, 1]]], np.int32))
     nq = U.ha_tile_shape(d)[2]
     blocks = 1 * 2 * nq
-    base = nbytes(d, HA_SPLIT_PARTS=1)
+    base = nbytes(d, split_parts=1)
     for cus in (8, 256):
-        assert nbytes(d, HA_SPLIT_PARTS=3, HA_CU_COUNT=cus) - base == plan_bytes(d, 3 * blocks, blocks,
+        assert nbytes(d, split_parts=3, plan_cus=cus) - base == plan_bytes(d, 3 * blocks, blocks,
                                                                                3 * blocks)
 
 
 def test_fp32_never_split():
     d = U.AttnDesc(1, 80, 4, 1, 64, "f32", np.array([[[0, 16, 0], [16, 64, 1]]], np.int32))
-    assert nbytes(d, HA_SPLIT_PARTS=4, HA_CU_COUNT=8) == nbytes(d, HA_SPLIT_PARTS=1)
+    assert nbytes(d, split_parts=4, plan_cus=8) == nbytes(d, split_parts=1)
 
 
 def test_per_batch_layouts_pad_the_table():
@@ -107,5 +99,5 @@ def test_per_batch_layouts_pad_the_table():
     them to the longest: 22 entries per XCD, 176 in all, 12 split blocks, 36 slots."""
     seg = np.array([[[0, 100, 0], [100, 900, 1]], [[0, 700, 0], [700, 300, 2]]], np.int32)
     d = U.AttnDesc(2, 1000, 16, 4, 128, "bf16", seg)
-    base = nbytes(d, HA_SPLIT_PARTS=1)
-    assert nbytes(d, HA_CU_COUNT=96) - base == plan_bytes(d, 176, 12, 36)
+    base = nbytes(d, split_parts=1)
+    assert nbytes(d, plan_cus=96) - base == plan_bytes(d, 176, 12, 36)

@@ -30,15 +30,16 @@ class HybridAttention:
 
     q [B][S][Hq][d], k/v [B][S][Hkv][d] contiguous bf16 or fp32 on the GPU. segments:
     int [B][n_seg][3] rows of (start, length, kind) with kind 0 causal, 1 full, 2 image
-    (generalized causal). rope: 'none', '1d', '2d' or 'mrope'; positions int32
-    [B][S][n_axes] on the GPU."""
+    (generalized causal), 3 Gen Image. rope: 'none', '1d', '2d' or 'mrope'; positions int32
+    [B][S][n_axes] on the GPU. split_parts and plan_cus override the forward's split planner
+    (ha_attn_desc)."""
 
     def __init__(self, batch, seq_len, n_q_heads, n_kv_heads, head_dim, dtype, segments,
                  rope="none", positions=None, theta=1e4, mrope_sections=(0, 0, 0),
                  q_norm_weight=None, k_norm_weight=None, eps=1e-6, scale=0.0, cos_sin=None,
-                 device="cuda"):
+                 device="cuda", split_parts=0, plan_cus=0):
         self.desc = B.AttnDesc(batch, seq_len, n_q_heads, n_kv_heads, head_dim, dtype, segments,
-                               scale)
+                               scale, split_parts=split_parts, plan_cus=plan_cus)
         self.shape = (batch, seq_len, n_q_heads, head_dim)
         self.pro = None
         prologue = rope != "none" or q_norm_weight is not None
@@ -136,11 +137,12 @@ class HybridAttention:
 
 def prefix_is_invariant(segments, seq_len: int, p: int) -> bool:
     """True when no query row below p attends to a key at or after p, in any batch item of
-    a segment table [B][n_seg][3] (start, length, kind: 0 causal, 1 full, 2 image): rows
-    below p then give the same output whatever tokens >= p hold. A causal row i sees keys
-    <= i, so causal segments never break it; a full segment's rows see every key, so one
-    that starts below p < seq_len does; an image segment's rows see keys below its end, so
-    one that p splits does."""
+    a segment table [B][n_seg][3] (start, length, kind: 0 causal, 1 full, 2 image, 3 Gen
+    Image): rows below p then give the same output whatever tokens >= p hold. A causal row i
+    sees keys <= i, so causal segments never break it; a full segment's rows see every key,
+    so one that starts below p < seq_len does; an image segment's rows (GCA or Gen Image) see
+    keys below its end, so one that p splits does. ha_attn_fwd_planned_from makes the same
+    check and refuses a row_begin that fails it."""
     if not 0 <= p <= seq_len:
         return False
     seg = np.asarray(segments, dtype=np.int64).reshape(-1, 3)
@@ -149,7 +151,7 @@ def prefix_is_invariant(segments, seq_len: int, p: int) -> bool:
             continue
         if kind == 1 and st < p < seq_len:
             return False
-        if kind == 2 and st < p < st + ln:
+        if kind in (2, 3) and st < p < st + ln:
             return False
     return True
 

@@ -46,7 +46,8 @@ class ha_attn_desc(ctypes.Structure):
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("segments", ctypes.POINTER(ha_segment)), ("n_segments", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("q_prescaled", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("q_prescaled", ctypes.c_int32),
+                ("split_parts", ctypes.c_int32), ("plan_cus", ctypes.c_int32)]
 
 
 class ha_prologue_desc(ctypes.Structure):
@@ -124,7 +125,7 @@ class AttnDesc:
     """Owns an ha_attn_desc and the host segment array it points to."""
 
     def __init__(self, batch, seq_len, n_q_heads, n_kv_heads, head_dim, dtype, segments,
-                 scale: float = 0.0, q_prescaled: int = 0):
+                 scale: float = 0.0, q_prescaled: int = 0, split_parts: int = 0, plan_cus: int = 0):
         seg = np.asarray(segments, dtype=np.int32)
         if batch > 0 and seq_len > 0:
             seg = np.ascontiguousarray(seg.reshape(batch, -1, 3))
@@ -138,7 +139,7 @@ class AttnDesc:
         dt = {"bf16": HA_DTYPE_BF16, "f32": HA_DTYPE_F32}.get(dtype, dtype)
         self.c = ha_attn_desc(batch, seq_len, n_q_heads, n_kv_heads, head_dim, dt,
                               ctypes.cast(self._seg, ctypes.POINTER(ha_segment)), n_seg,
-                              float(scale), int(q_prescaled))
+                              float(scale), int(q_prescaled), int(split_parts), int(plan_cus))
 
 
 class PrologueDesc:

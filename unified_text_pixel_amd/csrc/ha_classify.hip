@@ -135,7 +135,78 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- split plan table
+// One workgroup per XCD group x. Item j of the group is pair j / nq of the group (pairs x,
+// x + 8, ... when affine, else every pair) and query block nq - 1 - j % nq, with cost the
+// number of key tiles the classifier counted for that block. The list sorted by cost,
+// longest first and stable in j, has its positions [k, heavy) split into best parts of
+// ceil(cost / best) tiles; that list, sorted again the same way, is the group's final
+// order. A position's rank in a stable sort is the number of entries that sort before
+// it, counted directly (the lists hold at most kPlanMaxItems items; the parts of one item
+// stay adjacent because nothing lies between them before the sort).
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  const int x = blockIdx.x, tid = threadIdx.x;
+  const int n = a.n[x], best = a.best[x], k = a.k[x], heavy = a.heavy[x];
+  __shared__ int cost[kPlanMaxItems], order[kPlanMaxItems], c1[kPlanMaxItems], mult[kPlanMaxItems];
+  auto pair_of = [&](int j) { return a.affine ? x + 8 * (j / a.nq) : j / a.nq; };
+  for (int j = tid; j < n; j += kPlanThreads) {
+    const int b = pair_of(j) / a.Hkv, qb = a.nq - 1 - j % a.nq;
+    cost[j] = a.cost[((int64_t)b * a.nq + qb) * 2 + 1];
+  }
+  __syncthreads();
+  for (int j = tid; j < n; j += kPlanThreads) {
+    const int cj = cost[j];
+    int r = 0;
+    for (int u = 0; u < n; ++u) r += (cost[u] > cj || (cost[u] == cj && u < j)) ? 1 : 0;
+    order[r] = j;
+  }
+  __syncthreads();
+  for (int r = tid; r < n; r += kPlanThreads) {
+    const bool split = best > 1 && r >= k && r < heavy;
+    const int c = cost[order[r]];
+    c1[r] = split ? (c + best - 1) / best : c;
+    mult[r] = split ? best : 1;
+  }
+  __syncthreads();
+  for (int r = tid; r < n; r += kPlanThreads) {
+    const int cr = c1[r];
+    int f = 0;  // entries of the final list before this item's first part
+    for (int u = 0; u < n; ++u) f += (c1[u] > cr || (c1[u] == cr && u < r)) ? mult[u] : 0;
+    const int j = order[r];
+    const int bg = pair_of(j), qb = a.nq - 1 - j % a.nq;
+    const bool split = mult[r] > 1;
+    const int slot0 = split ? a.slot_base[x] + (r - k) * best : -1;
+    for (int p = 0; p < mult[r]; ++p) {
+      if (f + p >= a.len[x]) break;  // cannot happen: the list holds exactly len entries
+      int32_t* e = a.items + ((int64_t)(f + p) * a.groups + x) * 4;
+      e[0] = bg;
+      e[1] = qb;
+      e[2] = split ? (p | (best << 16)) : (1 << 16);
+      e[3] = split ? slot0 + p : -1;
+    }
+    if (split) {
+      int32_t* sp = a.splits + (int64_t)(a.split_base[x] + r - k) * 4;
+      sp[0] = bg;
+      sp[1] = qb;
+      sp[2] = slot0;
+      sp[3] = best;
+    }
+  }
+  for (int f = a.len[x] + tid; f < a.longest; f += kPlanThreads) {  // padding of shorter lists
+    int32_t* e = a.items + ((int64_t)f * a.groups + x) * 4;
+    e[0] = -1;
+    e[1] = e[2] = e[3] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(a.groups), dim3(kPlanThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_classify(const ClassifyArgs& a, hipStream_t stream) {
   dim3 grid(a.nq, a.seg.n_items);

@@ -15,7 +15,6 @@
 #include <cstdlib>
 #include <cstring>
 #include <functional>
-#include <mutex>
 #include <queue>
 #include <string>
 #include <vector>
@@ -41,12 +40,10 @@ ha_status ok() {
   return HA_OK;
 }
 
+// HA_DEBUG=1, read at each call: synchronise after every launch and check positions
 bool debug_sync() {
-  static const bool on = [] {
-    const char* e = std::getenv("HA_DEBUG");
-    return e && e[0] == '1';
-  }();
-  return on;
+  const char* e = std::getenv("HA_DEBUG");
+  return e && e[0] == '1';
 }
 
 ha_status check_launch(hipError_t e, hipStream_t stream, const char* what) {
@@ -87,6 +84,9 @@ ha_status check_desc(const ha_attn_desc* d) {
     return fail(HA_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if (d->q_prescaled != 0 && d->q_prescaled != 1)
     return fail(HA_ERR_INVALID_ARG, "q_prescaled must be 0 or 1");
+  if (d->split_parts < 0 || d->split_parts > 64)
+    return fail(HA_ERR_INVALID_ARG, "split_parts %d outside [0, 64]", d->split_parts);
+  if (d->plan_cus < 0) return fail(HA_ERR_INVALID_ARG, "plan_cus %d must be >= 0", d->plan_cus);
   if ((int64_t)d->n_q_heads * d->head_dim * (int64_t)d->seq_len * (d->batch ? d->batch : 1) >
       (int64_t(1) << 40))
     return fail(HA_ERR_UNSUPPORTED, "tensor too large");
@@ -267,9 +267,28 @@ ha_status run_prologue(const ha_attn_desc* d, const ha_prologue_desc* p, const v
   return check_launch(ha::launch_prologue(a, stream), stream, "prologue");
 }
 
+// HA_DEBUG: every rotary position of the call in [0, n_pos), checked on the device before
+// any kernel reads it (the positions of all batch items and tokens; a caller reusing a
+// prefix passes the same table). Without HA_DEBUG nothing is launched here.
+ha_status check_positions_debug(const ha_attn_desc* d, const ha_prologue_desc* p, hipStream_t stream) {
+  if (!p || p->rope_kind == HA_ROPE_NONE || !debug_sync() || empty(d)) return HA_OK;
+  const int64_t count = (int64_t)d->batch * d->seq_len * n_axes_of(p->rope_kind);
+  int64_t bad = -1;
+  int32_t value = 0;
+  const hipError_t e = ha::check_positions(p->positions, count, p->n_pos, stream, &bad, &value);
+  if (e != hipSuccess) return fail(HA_ERR_HIP, "position check failed: %s", hipGetErrorString(e));
+  if (bad >= 0) {
+    const int A = n_axes_of(p->rope_kind);
+    const int64_t tok = bad / A;
+    return fail(HA_ERR_INVALID_ARG, "positions[%lld][%lld][%d] = %d outside [0, n_pos %d)",
+                (long long)(tok / d->seq_len), (long long)(tok % d->seq_len), (int)(bad % A), value, p->n_pos);
+  }
+  return HA_OK;
+}
+
 // split query blocks on the device (null items: one work item per query block)
 struct SplitRun {
-  const int32_t* items = nullptr;
+  int32_t* items = nullptr;
   int n_items = 0;
   float* part_o = nullptr;
   float* part_l = nullptr;
@@ -324,16 +343,9 @@ ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const vo
 // it picks the part count by simulating list scheduling (the hardware dispatches in table
 // order to the CU that frees up first). A merge kernel combines the parts.
 
-// a positive integer from the environment, else 0
-int env_int(const char* name) {
-  const char* e = std::getenv(name);
-  const int v = e ? std::atoi(e) : 0;
-  return v > 0 ? v : 0;
-}
-
-// CUs of the current device (HA_CU_COUNT overrides it, for tests of the split path)
-int device_cus() {
-  if (const int v = env_int("HA_CU_COUNT")) return v;
+// CUs the planner balances over: desc->plan_cus, else the current device's count
+int plan_cus(const ha_attn_desc* d) {
+  if (d->plan_cus > 0) return d->plan_cus;
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
@@ -343,38 +355,22 @@ int device_cus() {
   return n;
 }
 
+// The host's part of a split plan: per XCD group, how many items it has, which positions of
+// its cost-sorted list are split and into how many parts, and where its slots and split
+// table rows start. The device builds the table itself (ha::launch_plan).
 struct SplitPlan {
   bool active = false;
+  int groups = 0, affine = 0, longest = 0;
   int n_items = 0, n_slots = 0, n_splits = 0;
-  std::vector<int32_t> items;   // [n_items][4]: b * Hkv + g (or -1), block, part | parts << 16, slot
-  std::vector<int32_t> splits;  // [n_splits][4]: b * Hkv + g, block, first slot, parts
+  int n[ha::kPlanGroups] = {}, best[ha::kPlanGroups] = {}, k[ha::kPlanGroups] = {};
+  int heavy[ha::kPlanGroups] = {}, slot_base[ha::kPlanGroups] = {}, split_base[ha::kPlanGroups] = {};
+  int len[ha::kPlanGroups] = {};
 };
-
-// The item and split tables reach the device by an asynchronous copy from pinned host
-// memory, which must outlive the copy: each distinct table is kept, unchanged, until the
-// process ends (a layout that repeats reuses its copy). Past kMaxTables distinct tables
-// the planner is not used (nullptr).
-constexpr size_t kMaxTables = 256;
-const int32_t* pinned_table(const std::vector<int32_t>& v) {
-  static std::mutex mu;
-  static std::vector<std::pair<std::vector<int32_t>, int32_t*>> kept;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const auto& e : kept)
-    if (e.first == v) return e.second;
-  if (kept.size() >= kMaxTables) return nullptr;
-  void* p = nullptr;
-  if (hipHostMalloc(&p, std::max<size_t>(v.size(), 1) * 4, hipHostMallocDefault) != hipSuccess || !p) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  std::memcpy(p, v.data(), v.size() * 4);
-  kept.emplace_back(v, static_cast<int32_t*>(p));
-  return kept.back().second;
-}
 
 // Key tiles each query block of batch item b executes, from the segment table: the tiles
 // before its rows' largest key limit, less, with Gen Images, the tiles whose every key is
-// hidden from the block's first row (the tile classifier's SKIP rule).
+// hidden from the block's first row (the tile classifier's SKIP rule, so these are the
+// counts the classifier writes and the device plan sorts by).
 std::vector<int> block_costs(const ha_attn_desc* d, int b, int bq, int nq, int nk) {
   const int S = d->seq_len, bk = ha::kBlockK;
   const ha_segment* seg = d->segments + (int64_t)b * d->n_segments;
@@ -420,101 +416,87 @@ double list_schedule(const std::vector<double>& costs, int n) {
   return ms;
 }
 
-// HA_SPLIT_PARTS (for tests): 1 never splits, P > 1 splits every query block into P parts.
+// desc->split_parts: 1 never splits, P > 1 splits every query block into P parts.
 SplitPlan plan_split(const ha_attn_desc* d) {
   SplitPlan plan;
   if (d->dtype != HA_DTYPE_BF16 || empty(d)) return plan;
-  const int force = std::min(env_int("HA_SPLIT_PARTS"), 64);
+  const int force = d->split_parts;
   if (force == 1) return plan;
-  const int n_cus = device_cus();
+  const int n_cus = plan_cus(d);
   if (n_cus <= 0) return plan;
   int bq, bk, nq, nk;
   tile_shape(d, &bq, &bk, &nq, &nk);
   const int nbg = d->batch * d->n_kv_heads;
   const bool affine = nbg % 8 == 0;  // the unsplit order keeps each pair on one XCD
   const int groups = affine ? 8 : 1;
+  if ((int64_t)(nbg / groups) * nq > ha::kPlanMaxItems) return plan;  // the device sort's limit
   const int cus = std::max(1, affine ? n_cus / 8 : n_cus);
   constexpr double kItem = 4.0;  // fixed cost of a work item (start, last tile, stores), in tiles
-  struct E {
-    int bg, qb, cost, part, parts, slot;
-  };
-  std::vector<std::vector<E>> lists(groups);
   std::vector<int> cost;  // of batch item cost_b
   int cost_b = -1;
-  int slot = 0;
+  int slot = 0, n_splits = 0, longest = 0;
   for (int x = 0; x < groups; ++x) {
-    std::vector<E> it;
+    std::vector<int> it;  // costs in the group's item order: pairs x, x + 8, ..., blocks from the last
     for (int bg = affine ? x : 0; bg < nbg; bg += affine ? 8 : 1) {
       const int b = bg / d->n_kv_heads;
       if (b != cost_b) {
         cost = block_costs(d, b, bq, nq, nk);
         cost_b = b;
       }
-      for (int qb = nq - 1; qb >= 0; --qb) it.push_back({bg, qb, cost[qb], 0, 1, -1});
+      for (int qb = nq - 1; qb >= 0; --qb) it.push_back(cost[qb]);
     }
-    std::stable_sort(it.begin(), it.end(), [](const E& p, const E& q) { return p.cost > q.cost; });
-    if (it.empty()) continue;
-    const int cmax = it[0].cost;
-    int heavy = 0;
-    while (heavy < (int)it.size() && 4 * it[heavy].cost >= 3 * cmax) ++heavy;
-    int k = heavy / cus * cus;  // the heavy items that fill whole rounds stay whole
-    if (force > 1) {
-      k = 0;
-      heavy = (int)it.size();
-    }
-    int best = 1;
-    double best_ms = 0.0, whole_ms = 0.0;
-    for (int parts : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
-      if (force > 1 || (parts > 1 && (k == heavy || parts > cmax))) break;
-      std::vector<double> c;
-      for (int i = 0; i < (int)it.size(); ++i) {
-        const bool split = parts > 1 && i >= k && i < heavy;
-        for (int p = 0; p < (split ? parts : 1); ++p)
-          c.push_back((split ? std::ceil((double)it[i].cost / parts) : (double)it[i].cost) + kItem);
-      }
-      std::stable_sort(c.begin(), c.end(), std::greater<double>());
-      const double ms = list_schedule(c, cus) + (parts > 1 ? kItem : 0.0);  // + the merge
-      if (parts == 1) whole_ms = ms;
-      if (parts == 1 || ms < best_ms) {
-        best = parts;
-        best_ms = ms;
-      }
-    }
-    if (best_ms > 0.97 * whole_ms) best = 1;  // not worth a merge
-    if (force > 1) best = force;
-    std::vector<E>& out = lists[x];
-    for (int i = 0; i < (int)it.size(); ++i) {
-      if (best > 1 && i >= k && i < heavy) {
-        plan.splits.insert(plan.splits.end(), {it[i].bg, it[i].qb, slot, best});
-        for (int p = 0; p < best; ++p)
-          out.push_back({it[i].bg, it[i].qb, (it[i].cost + best - 1) / best, p, best, slot + p});
-        slot += best;
+    std::stable_sort(it.begin(), it.end(), std::greater<int>());
+    const int n = (int)it.size();
+    int best = 1, k = 0, heavy = 0;
+    if (n > 0) {
+      const int cmax = it[0];
+      while (heavy < n && 4 * it[heavy] >= 3 * cmax) ++heavy;
+      k = heavy / cus * cus;  // the heavy items that fill whole rounds stay whole
+      if (force > 1) {
+        k = 0;
+        heavy = n;
+        best = force;
       } else {
-        out.push_back(it[i]);
+        double best_ms = 0.0, whole_ms = 0.0;
+        for (int parts : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
+          if (parts > 1 && (k == heavy || parts > cmax)) break;
+          std::vector<double> c;
+          for (int i = 0; i < n; ++i) {
+            const bool split = parts > 1 && i >= k && i < heavy;
+            for (int p = 0; p < (split ? parts : 1); ++p)
+              c.push_back((split ? std::ceil((double)it[i] / parts) : (double)it[i]) + kItem);
+          }
+          std::stable_sort(c.begin(), c.end(), std::greater<double>());
+          const double ms = list_schedule(c, cus) + (parts > 1 ? kItem : 0.0);  // + the merge
+          if (parts == 1) whole_ms = ms;
+          if (parts == 1 || ms < best_ms) {
+            best = parts;
+            best_ms = ms;
+          }
+        }
+        if (best_ms > 0.97 * whole_ms) best = 1;  // not worth a merge
       }
     }
-    std::stable_sort(out.begin(), out.end(), [](const E& p, const E& q) { return p.cost > q.cost; });
+    plan.n[x] = n;
+    plan.best[x] = best;
+    plan.k[x] = k;
+    plan.heavy[x] = heavy;
+    plan.slot_base[x] = slot;
+    plan.split_base[x] = n_splits;
+    plan.len[x] = best > 1 ? n + (heavy - k) * (best - 1) : n;
+    if (best > 1) {
+      slot += (heavy - k) * best;
+      n_splits += heavy - k;
+    }
+    longest = std::max(longest, plan.len[x]);
   }
   if (slot == 0) return plan;  // nothing to split: the unsplit order is as good
-  size_t longest = 0;
-  for (const auto& l : lists) longest = std::max(longest, l.size());
-  plan.n_items = (int)(longest * groups);
-  plan.items.assign((size_t)plan.n_items * 4, 0);
-  for (int i = 0; i < plan.n_items; ++i) {
-    const auto& l = lists[i % groups];
-    const size_t at = (size_t)(i / groups);
-    int32_t* e = &plan.items[(size_t)i * 4];
-    if (at < l.size()) {
-      e[0] = l[at].bg;
-      e[1] = l[at].qb;
-      e[2] = l[at].part | (l[at].parts << 16);
-      e[3] = l[at].slot;
-    } else {
-      e[0] = -1;  // padding
-    }
-  }
+  plan.groups = groups;
+  plan.affine = affine ? 1 : 0;
+  plan.longest = longest;
+  plan.n_items = longest * groups;
   plan.n_slots = slot;
-  plan.n_splits = (int)(plan.splits.size() / 4);
+  plan.n_splits = n_splits;
   plan.active = true;
   return plan;
 }
@@ -691,6 +673,7 @@ ha_status ha_qk_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro, 
   if ((st = check_tensor(q_in, "q_in")) != HA_OK || (st = check_tensor(k_in, "k_in")) != HA_OK ||
       (st = check_tensor(q_out, "q_out")) != HA_OK || (st = check_tensor(k_out, "k_out")) != HA_OK)
     return st;
+  if ((st = check_positions_debug(desc, pro, static_cast<hipStream_t>(stream))) != HA_OK) return st;
   st = run_prologue(desc, pro, q_in, k_in, q_out, k_out, pro->q_out_scale > 0.f ? pro->q_out_scale : 1.f,
                     static_cast<hipStream_t>(stream));
   return st == HA_OK ? ok() : st;
@@ -722,6 +705,12 @@ ha_status ha_attn_fwd_planned(const ha_attn_desc* desc, const void* q, const voi
 
 namespace {
 
+// The forward after validation, with the workspace already checked against the layout w
+// of plan (both as attn_fwd chose them).
+ha_status attn_fwd_run(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
+                       const void* v, void* out, float* lse, void* workspace, const SplitPlan& plan,
+                       const Workspace& w, void* stream);
+
 ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
                    const void* v, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   ha_status st = check_desc(desc);
@@ -735,17 +724,18 @@ ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const 
   // gives), else one work item per query block
   SplitPlan plan = plan_split(desc);
   Workspace w = workspace_layout(desc, pro != nullptr, plan);
-  const int32_t* table = nullptr;
-  if (plan.active && workspace_bytes >= w.total) {
-    std::vector<int32_t> both = plan.items;
-    both.insert(both.end(), plan.splits.begin(), plan.splits.end());
-    table = pinned_table(both);
-  }
-  if (!table) {
+  if (plan.active && workspace_bytes < w.total) {
     plan = SplitPlan{};
     w = workspace_layout(desc, pro != nullptr);
   }
   if ((st = check_workspace(workspace, workspace_bytes, w.total)) != HA_OK) return st;
+  return attn_fwd_run(desc, pro, q, k, v, out, lse, workspace, plan, w, stream);
+}
+
+ha_status attn_fwd_run(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q, const void* k,
+                       const void* v, void* out, float* lse, void* workspace, const SplitPlan& plan,
+                       const Workspace& w, void* stream) {
+  ha_status st = HA_OK;
   char* ws = static_cast<char*>(workspace);
   int32_t* row_limit = reinterpret_cast<int32_t*>(ws + w.row_limit);
   int32_t* ranges = reinterpret_cast<int32_t*>(ws + w.ranges);
@@ -758,12 +748,33 @@ ha_status attn_fwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, const 
     split.part_o = reinterpret_cast<float*>(ws + w.part_o);
     split.part_l = reinterpret_cast<float*>(ws + w.part_l);
     split.part_m = reinterpret_cast<float*>(ws + w.part_m);
-    const size_t bytes = (size_t)(plan.n_items + plan.n_splits) * 16;
-    if ((st = check_launch(hipMemcpyAsync(ws + w.items, table, bytes, hipMemcpyHostToDevice, s), s,
-                           "item table copy")) != HA_OK)
-      return st;
   }
+  if ((st = check_positions_debug(desc, pro, s)) != HA_OK) return st;
   if ((st = run_classify(desc, nullptr, ranges, row_limit, s, hole)) != HA_OK) return st;
+  if (plan.active) {
+    // the work item table, from the tile counts the classifier just wrote
+    ha::PlanArgs pa{};
+    int bq, bk, nq, nk;
+    tile_shape(desc, &bq, &bk, &nq, &nk);
+    pa.cost = hole.tile_count ? hole.tile_count : ranges;
+    pa.items = split.items;
+    pa.splits = split.items + (size_t)plan.n_items * 4;
+    pa.nq = nq;
+    pa.Hkv = desc->n_kv_heads;
+    pa.groups = plan.groups;
+    pa.affine = plan.affine;
+    pa.longest = plan.longest;
+    for (int x = 0; x < plan.groups; ++x) {
+      pa.n[x] = plan.n[x];
+      pa.best[x] = plan.best[x];
+      pa.k[x] = plan.k[x];
+      pa.heavy[x] = plan.heavy[x];
+      pa.slot_base[x] = plan.slot_base[x];
+      pa.split_base[x] = plan.split_base[x];
+      pa.len[x] = plan.len[x];
+    }
+    if ((st = check_launch(ha::launch_plan(pa, s), s, "split plan table")) != HA_OK) return st;
+  }
   const void* qa = q;
   const void* ka = k;
   if (pro) {
@@ -812,6 +823,7 @@ ha_status ha_qk_prologue_from(const ha_attn_desc* desc, const ha_prologue_desc* 
   if ((st = check_tensor(q_in, "q_in")) != HA_OK || (st = check_tensor(k_in, "k_in")) != HA_OK ||
       (st = check_tensor(q_out, "q_out")) != HA_OK || (st = check_tensor(k_out, "k_out")) != HA_OK)
     return st;
+  if ((st = check_positions_debug(desc, pro, static_cast<hipStream_t>(stream))) != HA_OK) return st;
   st = run_prologue(desc, pro, q_in, k_in, q_out, k_out, pro->q_out_scale > 0.f ? pro->q_out_scale : 1.f,
                     static_cast<hipStream_t>(stream), token_begin);
   return st == HA_OK ? ok() : st;
@@ -833,6 +845,20 @@ ha_status ha_attn_fwd_planned_from(const ha_attn_desc* desc, const void* q, cons
     return fail(HA_ERR_ALIGNMENT, "row_limit and ranges must be 4-byte aligned");
   if (has_gen(desc))
     return fail(HA_ERR_UNSUPPORTED, "Gen Image segments need the full tile plan: use ha_attn_fwd");
+  // the rows kept from an earlier step must not see keys at or after row_begin: a causal
+  // row sees keys up to itself, a full row every key, an image row keys up to its
+  // segment's end
+  for (int b = 0; b < desc->batch; ++b)
+    for (int t = 0; t < desc->n_segments; ++t) {
+      const ha_segment& g = desc->segments[(int64_t)b * desc->n_segments + t];
+      const int end = g.start + g.length;
+      if ((g.kind == HA_SEG_FULL && g.start < row_begin && row_begin < desc->seq_len) ||
+          ((g.kind == HA_SEG_GCA || g.kind == HA_SEG_GEN) && g.start < row_begin && row_begin < end))
+        return fail(HA_ERR_INVALID_ARG,
+                    "row_begin %d: rows of batch %d segment %d (kind %d, [%d, %d)) below it attend to keys at or "
+                    "after it",
+                    row_begin, b, t, g.kind, g.start, end);
+    }
   st = run_attn(desc, q, k, v, row_limit, ranges, out, desc->q_prescaled == 1, static_cast<hipStream_t>(stream),
                 nullptr, row_begin);
   return st == HA_OK ? ok() : st;
@@ -891,6 +917,7 @@ ha_status ha_qkv_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
     a.wk = pro->k_norm_weight;
     a.eps = pro->eps;
   }
+  if ((st = check_positions_debug(desc, pro, static_cast<hipStream_t>(stream))) != HA_OK) return st;
   int dev = 0, n_cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
@@ -946,6 +973,7 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   float* dk_rot = reinterpret_cast<float*>(ws + w.dk_rot);
 
   const HolePlan hole = hole_plan(desc, ws, w.key_vis, w.tiles, w.tile_count);
+  if ((st = check_positions_debug(desc, pro, s)) != HA_OK) return st;
   if ((st = run_classify(desc, nullptr, ranges, row_limit, s, hole)) != HA_OK) return st;
   // q' = scale log2(e) (normalised, rotated q) and the rotated k, as the forward used them
   ha_prologue_desc plain{};

@@ -40,6 +40,27 @@ struct ClassifyArgs {
 };
 hipError_t launch_classify(const ClassifyArgs& a, hipStream_t stream);
 
+// Work item table of a split plan, built on the device from the classifier's per-block tile
+// counts. The host decides per XCD group x (8 groups when the (batch, KV head) pairs split
+// evenly over the XCDs, else 1) which items of the group's list, sorted longest first, are
+// split and into how many parts; the kernel sorts (stably, by tile count) and writes the
+// table: entry e of the table is (b * Hkv + g, query block, part | parts << 16, slot or -1),
+// item f of group x's final list at entry f * groups + x, -1 rows as padding; then the
+// split table [n_splits][4] of (b * Hkv + g, query block, first slot, parts).
+constexpr int kPlanGroups = 8;
+constexpr int kPlanMaxItems = 1024;  // items per group before splitting
+struct PlanArgs {
+  const int32_t* cost;  // [B][nq][2]: field 1 is the number of key tiles the block executes
+  int32_t* items;       // [longest * groups][4]
+  int32_t* splits;      // [n_splits][4]
+  int32_t nq, Hkv, groups, affine, longest;
+  // per group: items n (pairs of the group x nq), split parts best (1: none), sorted
+  // positions [k, heavy) split, first slot and first split-table row, final list length
+  int32_t n[kPlanGroups], best[kPlanGroups], k[kPlanGroups], heavy[kPlanGroups];
+  int32_t slot_base[kPlanGroups], split_base[kPlanGroups], len[kPlanGroups];
+};
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+
 struct PrologueArgs {
   const void* q_in;
   const void* k_in;
@@ -58,6 +79,11 @@ struct PrologueArgs {
   uint8_t axis[64];  // rotary axis of pair i
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
+
+// Debug check of rotary positions (HA_DEBUG): the first index of positions[0, count) outside
+// [0, n_pos), or -1, and the value found there. Synchronises the stream.
+hipError_t check_positions(const int32_t* positions, int64_t count, int32_t n_pos, hipStream_t stream,
+                           int64_t* first_bad, int32_t* value);
 
 // Attention tile shape: block_q query tokens per work item, kBlockK keys per tile.
 constexpr int kBlockK = 64;

@@ -10,6 +10,8 @@
 // threads per head row each own 8 pairs, i.e. elements [8c, 8c+8) and [D/2+8c, D/2+8c+8),
 // which are 16-byte (bf16) loads and stores. The row's mean square is reduced across
 // those D/16 lanes. fp32 math throughout; bf16 results are rounded to nearest even.
+#include <algorithm>
+
 #include "ha_internal.h"
 
 namespace ha {
@@ -259,6 +261,47 @@ hipError_t launch_dw_reduce(const float* part, int64_t n, int D, float* scratch,
   hipLaunchKernelGGL(dw_sum_kernel, dim3(1), dim3(1024), 0, stream, (const float*)scratch, (int64_t)kDwBlocks, D,
                      dw);
   return hipGetLastError();
+}
+
+}  // namespace ha
+
+// ====================================================================== debug position check
+// HA_DEBUG only: the first position outside [0, n_pos), found with a 64-bit atomic minimum
+// over the flat index (the kernels themselves clamp positions to that range).
+namespace ha {
+namespace {
+
+__device__ unsigned long long g_first_bad_position;
+
+__global__ void reset_position_check() { g_first_bad_position = ~0ull; }
+
+__global__ __launch_bounds__(256) void position_check_kernel(const int32_t* pos, int64_t count, int32_t n_pos) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t v = pos[i];
+    if (v < 0 || v >= n_pos) atomicMin(&g_first_bad_position, (unsigned long long)i);
+  }
+}
+
+}  // namespace
+
+hipError_t check_positions(const int32_t* positions, int64_t count, int32_t n_pos, hipStream_t stream,
+                           int64_t* first_bad, int32_t* value) {
+  *first_bad = -1;
+  *value = 0;
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reset_position_check, dim3(1), dim3(1), 0, stream);
+  const int64_t blocks = std::min<int64_t>((count + 255) / 256, 1024);
+  hipLaunchKernelGGL(position_check_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, positions, count, n_pos);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  unsigned long long bad = 0;
+  e = hipMemcpyFromSymbolAsync(&bad, HIP_SYMBOL(g_first_bad_position), sizeof bad, 0, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess || bad == ~0ull) return e;
+  *first_bad = (int64_t)bad;
+  e = hipMemcpyAsync(value, positions + bad, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return e;
 }
 
 }  // namespace ha
