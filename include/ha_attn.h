@@ -284,6 +284,22 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
                       const void* dout, void* dq, void* dk, void* dv, float* dw_q, float* dw_k,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- allocation-free forward
+ * For callers that cannot allocate: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. ha_attn_fwd with pro == NULL (q, k already normalised and
+ * rotated; plain or prescaled q as desc->q_prescaled says, like ha_attn_fwd_planned), but
+ * its scratch (row limits, tile ranges, Gen Image plan, split plan table and partial
+ * results) lives in a device array of the library, HA_STATIC_SCRATCH_BYTES per GPU, held
+ * from the library's first use on that GPU until the process ends. The call allocates
+ * nothing and calls no allocating routine. A problem whose scratch exceeds the array (with
+ * the split plan if it fits, else without it) fails with HA_ERR_WORKSPACE before any launch.
+ * Every call on a GPU shares that GPU's array and overwrites what it reads before reading
+ * it; calls that overlap on one GPU (two streams, two threads) race and must be ordered by
+ * the caller. Results equal ha_attn_fwd's bit for bit. */
+#define HA_STATIC_SCRATCH_BYTES (16u << 20)
+ha_status ha_attn_fwd_static(const ha_attn_desc* desc, const void* q, const void* k, const void* v,
+                             void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

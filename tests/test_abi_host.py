@@ -25,7 +25,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = U.load_library()
     names = declared_functions()
-    assert len(names) == 16 and sorted(B.EXPORTS) == names
+    assert len(names) == 17 and sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
     assert U.ha_abi_version() == 5
@@ -80,6 +80,7 @@ def test_bad_descriptor_rejected_everywhere(kw, status, text):
         lambda: U.ha_attn_bwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                               FAKE, 1 << 30, stream=0),
         lambda: U.ha_qkv_prologue(d, None, FAKE, 256, FAKE, FAKE, FAKE, FAKE, stream=0),
+        lambda: U.ha_attn_fwd_static(d, FAKE, FAKE, FAKE, FAKE, stream=0),
     ]
     for call in calls:
         with pytest.raises(U.HAError) as e:
@@ -323,4 +324,19 @@ def test_qkv_projection_rejects_before_launch():
     # no tokens: nothing to do, no launch
     U.ha_qkv_prologue(bf16_desc(batch=0, segments=np.zeros((0, 0, 3))), None, None, 256, None, None, None, None,
                       stream=0)
+    assert U.ha_last_error() == ""
+
+
+def test_static_forward_rejects_before_launch():
+    """ha_attn_fwd_static: bad pointers, and a problem whose scratch exceeds the library's
+    16 MiB array (row limits alone: 4 bytes a token, 8 x 600,000 tokens), fail on the host."""
+    with pytest.raises(U.HAError) as e:
+        U.ha_attn_fwd_static(desc(), None, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.HA_ERR_INVALID_ARG and "q is NULL" in str(e.value)
+    S = 600_000
+    big = U.AttnDesc(8, S, 8, 2, 128, "bf16", np.array([[[0, S, 0]]] * 8, np.int32))
+    with pytest.raises(U.HAError) as e:
+        U.ha_attn_fwd_static(big, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.HA_ERR_WORKSPACE and "static array holds 16777216" in str(e.value)
+    U.ha_attn_fwd_static(desc(batch=0, segments=np.zeros((0, 0, 3))), None, None, None, None, stream=0)
     assert U.ha_last_error() == ""

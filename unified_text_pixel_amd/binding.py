@@ -28,7 +28,8 @@ ROPE_KINDS = {"none": HA_ROPE_NONE, "1d": HA_ROPE_1D, "2d": HA_ROPE_2D, "mrope":
 EXPORTS = ("ha_abi_version", "ha_last_error", "ha_rope_table_fill", "ha_q_prescale",
            "ha_tile_shape", "ha_classify_tiles", "ha_qk_prologue", "ha_attn_workspace_bytes",
            "ha_attn_fwd_planned", "ha_attn_fwd", "ha_attn_fwd_lse", "ha_attn_bwd_workspace_bytes",
-           "ha_attn_bwd", "ha_qk_prologue_from", "ha_attn_fwd_planned_from", "ha_qkv_prologue")
+           "ha_attn_bwd", "ha_qk_prologue_from", "ha_attn_fwd_planned_from", "ha_qkv_prologue",
+           "ha_attn_fwd_static")
 
 
 class HAError(RuntimeError):
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
         "ha_qk_prologue_from": ([D, PD, P, P, P, P, I32, P], ctypes.c_int),
         "ha_attn_fwd_planned_from": ([D, P, P, P, P, P, P, I32, P], ctypes.c_int),
         "ha_qkv_prologue": ([D, PD, P, I32, P, P, P, P, P], ctypes.c_int),
+        "ha_attn_fwd_static": ([D, P, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -257,3 +259,7 @@ def ha_attn_fwd_planned_from(desc: AttnDesc, q, k, v, row_limit, ranges, out, ro
 def ha_qkv_prologue(desc: AttnDesc, pro, x, hidden: int, w_qkv, q_out, k_out, v_out, stream=None):
     _check(load_library().ha_qkv_prologue(_d(desc), _pd(pro), _ptr(x), int(hidden), _ptr(w_qkv), _ptr(q_out),
                                           _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def ha_attn_fwd_static(desc: AttnDesc, q, k, v, out, stream=None):
+    _check(load_library().ha_attn_fwd_static(_d(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream)))

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libha.so")
-SOURCES = ["ha_host.cpp", "ha_classify.hip", "ha_prologue.hip", "ha_attn_fwd.hip", "ha_attn_bwd.hip", "ha_qkv.hip"]
+SOURCES = ["ha_host.cpp", "ha_classify.hip", "ha_prologue.hip", "ha_attn_fwd.hip", "ha_attn_bwd.hip", "ha_qkv.hip",
+           "ha_scratch.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]

@@ -879,6 +879,34 @@ ha_status ha_attn_fwd_lse(const ha_attn_desc* desc, const ha_prologue_desc* pro,
   return attn_fwd(desc, pro, q, k, v, out, lse, workspace, workspace_bytes, stream);
 }
 
+ha_status ha_attn_fwd_static(const ha_attn_desc* desc, const void* q, const void* k, const void* v, void* out,
+                             void* stream) {
+  ha_status st = check_desc(desc);
+  if (st != HA_OK) return st;
+  if (empty(desc)) return ok();
+  if ((st = check_tensor(q, "q")) != HA_OK || (st = check_tensor(k, "k")) != HA_OK ||
+      (st = check_tensor(v, "v")) != HA_OK || (st = check_tensor(out, "out")) != HA_OK)
+    return st;
+  // as ha_attn_fwd without a prologue: the split plan when the scratch array holds it, else
+  // one work item per query block, else the problem is too large for the array
+  SplitPlan plan = plan_split(desc);
+  Workspace w = workspace_layout(desc, false, plan);
+  if (plan.active && w.total > ha::kStaticScratchBytes) {
+    plan = SplitPlan{};
+    w = workspace_layout(desc, false);
+  }
+  if (w.total > ha::kStaticScratchBytes)
+    return fail(HA_ERR_WORKSPACE,
+                "ha_attn_fwd_static: this problem needs %zu bytes of scratch, the static array holds %zu "
+                "(use ha_attn_fwd with a workspace)",
+                w.total, ha::kStaticScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = ha::static_scratch(&scratch);
+  if (e != hipSuccess) return fail(HA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  st = attn_fwd_run(desc, nullptr, q, k, v, out, nullptr, scratch, plan, w, stream);
+  return st == HA_OK ? ok() : st;
+}
+
 ha_status ha_qkv_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* x, int32_t hidden,
                           const void* w_qkv, void* q_out, void* k_out, void* v_out, void* stream) {
   ha_status st = check_desc(desc);

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "ha_attn.h"
+
 namespace ha {
 
 // Segment tables of several batch items, passed by value as kernel arguments.
@@ -131,6 +133,12 @@ struct CombineArgs {
   int32_t n_splits, S, Hq, Hkv, nq, BQ, G, D;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// ---- allocation-free forward (ha_scratch.hip)
+// Bytes of the device-side scratch array; its address on the current device (looked up
+// once per device and kept).
+constexpr size_t kStaticScratchBytes = HA_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void** addr);
 
 // ---- QKV projection with the prologue in its epilogue (ha_qkv.hip)
 struct QkvArgs {
