@@ -392,6 +392,9 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     const char* const kr = PAR ? k0 : k1;  // K_{t+1}
     char* const vw = PAR ? v1 : v0;        // receives V_t
     const char* const vr = PAR ? v0 : v1;  // V_{t-1}
+    // publish whether a row of this wave has left the range; read, past the barrier, whether
+    // any wave has (the FAST loop stops at the end of the trip that sees it)
+    if (PAR == 1 && __builtin_amdgcn_ballot_w64(off_range)) redo = 1;
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (FAST || t + 2 < kend) dma.template tile<false, !FAST>(tile_at(t + 2) * BK, kw);
@@ -406,6 +409,9 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     const float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
     off_range = off_range || !(ts <= kHi) || !(l + ts >= kLo);
     l += ts;
+    // read past the barrier, at the end of the step: no wave publishes again before the
+    // next odd step's barrier, which every wave reaches only after this read
+    return PAR == 1 && __builtin_amdgcn_readfirstlane(redo) != 0;
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
@@ -430,18 +436,22 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // then even), the S registers alternating roles; sb holds S_t when a trip starts. (A
   // tile list puts the tiles that are full and inside the sequence first.)
   const int fast_end = LIST ? max(1, min(kfull, kend) - 2) : max(1, min(min(kfull, kend - 2), S / BK - t0 - 2));
+  // Once a row of the work item has left the range the main pass stops at the end of the
+  // FAST trip that sees it (the careful pass below starts over), so a work item that needs
+  // the careful pass wastes little of its main pass.
   step(std::false_type{}, P0{}, 0, sa, sb, pb, pa);  // S_1 -> sb, P_0 -> pa
   int t = 1;
-  for (; t + 1 < fast_end; t += 2) {
-    step(std::true_type{}, P1{}, t, sb, sa, pa, pb);      // S_{t+1} -> sa, P_t -> pb
-    step(std::true_type{}, P0{}, t + 1, sa, sb, pb, pa);  // S_{t+2} -> sb, P_{t+1} -> pa
+  bool left = false;
+  for (; t + 1 < fast_end && !left; t += 2) {
+    left = step(std::true_type{}, P1{}, t, sb, sa, pa, pb);  // S_{t+1} -> sa, P_t -> pb
+    step(std::true_type{}, P0{}, t + 1, sa, sb, pb, pa);     // S_{t+2} -> sb, P_{t+1} -> pa
   }
-  for (; t + 1 < kend; t += 2) {
+  for (; !left && t + 1 < kend; t += 2) {
     step(std::false_type{}, P1{}, t, sb, sa, pa, pb);
     step(std::false_type{}, P0{}, t + 1, sa, sb, pb, pa);
   }
-  if (t < kend) step(std::false_type{}, P1{}, t, sb, sa, pa, pb);
-  // last tile's P V
+  if (!left && t < kend) step(std::false_type{}, P1{}, t, sb, sa, pa, pb);
+  // last tile's P V (a main pass left early computes a P V the careful pass discards)
   if (__builtin_amdgcn_ballot_w64(off_range)) redo = 1;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -451,25 +461,37 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     pv(v0, pa);
 
   // Careful pass, only when some row of the work item left the range: every wave starts
-  // over, one tile at a time, and re-references rows whose tile sum leaves [kLo, kHi] to
-  // the larger of the tile max and log2(l), so both the old sum and the new tile end up
-  // <= 1 with one of them near 1. Numerator and denominator share the reference either
-  // way, so the result is the softmax up to rounding. negm holds -m in the units of the S
-  // accumulator (log2 units when q is prescaled, raw otherwise) and is the C operand of
-  // each tile's first MFMA.
+  // over and re-references rows whose tile sum leaves [kLo, kHi] to the larger of the tile
+  // max and log2(l), so both the old sum and the new tile end up <= 1 with one of them near
+  // 1. Numerator and denominator share the reference either way, so the result is the
+  // softmax up to rounding. negm holds -m in the units of the S accumulator (log2 units
+  // when q is prescaled, raw otherwise) and is the C operand of each tile's first MFMA.
+  // Tile u sits in buffer u mod 2 (compile-time parity) and tile u + 1's DMA runs while
+  // tile u is computed; past the last tile the DMA reloads the last tile into the free
+  // buffer, which nothing reads (a DMA behind a branch would make the compiler wait for
+  // every DMA in flight before the next LDS read).
   float mref = 0.f;  // the row's reference m (0 unless the careful pass moved it)
   if (redo) {
     f32x16 negm = f32x16{};
     l = 0.f;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
-    for (int u = 0; u < kend; ++u) {
-      __syncthreads();  // every wave is done with the buffers
-      dma.template tile<false, true>(tile_at(u) * BK, k0);
-      dma.template tile<true, true>(tile_at(u) * BK, v0);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave is done with the buffers
+    dma.template tile<false, true>(tile_at(0) * BK, k0);
+    dma.template tile<true, true>(tile_at(0) * BK, v0);
+    auto cstep = [&](auto par_tag, int u) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par_tag)::value;
+      const char* const kb = PAR ? k1 : k0;
+      const char* const vb = PAR ? v1 : v0;
+      char* const kn = PAR ? k0 : k1;
+      char* const vn = PAR ? v0 : v1;
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      const auto s0 = qk(k0, negm);
+      __syncthreads();  // tile u landed; every wave is done with tile u - 1's buffers
+      const int un = min(u + 1, kend - 1);
+      dma.template tile<false, true>(tile_at(un) * BK, kn);
+      dma.template tile<true, true>(tile_at(un) * BK, vn);
+      const auto s0 = qk(kb, negm);
       f32x16 sc[2] = {s0[0], s0[1]};
       mask(sc, u);
       float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pa));
@@ -501,8 +523,14 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
         ts = wave_pair_sum(exp_tile<PRE>(sc, c, pa));
       }
       l += ts;
-      pv(v0, pa);
+      pv(vb, pa);
+    };
+    int u = 0;
+    for (; u + 1 < kend; u += 2) {
+      cstep(P0{}, u);
+      cstep(P1{}, u + 1);
     }
+    if (u < kend) cstep(P0{}, u);
   }
 
   // a part of a split query block: its unnormalised output, row sum and row reference
