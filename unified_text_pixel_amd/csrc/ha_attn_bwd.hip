@@ -293,8 +293,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
 
   auto compute = [&](const char* qc, const char* oc, float lr, float dr, int mr, int s, bool masked)
                      __attribute__((always_inline)) {
-    // the lane's LDS addresses are rebuilt each step from an opaque copy of the lane id:
-    // kept live across the loop they would not fit in registers
+    // LDS addresses: a tile row's 16-byte chunk c sits at chunk c ^ swz(row), and the row
+    // offset occupies the bits above the chunk, so the operand of k-step kk is at the
+    // lane's k-step-0 offset XOR 32 kk. The per-lane offsets are rebuilt each step from an
+    // opaque copy of the lane id (kept live across the loop they would not fit).
     int lo = lane;
     __asm__ volatile("" : "+v"(lo));
     const int lnx = lo & 31, hix = lo >> 5;
@@ -303,54 +305,94 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
     f32x16 sacc = mfma(split_col(lr * kLog2e), ones, f32x16{});
     f32x16 pacc = mfma(split_col(dr), ones, f32x16{});
     if (qrow0 + 32 * s + ln < 0) mr = 0;  // rows before the sequence see no key
-    const char* qrow = qc + (lnx * G + hg) * (2 * D);
-    const char* orow = oc + (lnx * G + hg) * (2 * D);
-    const char* krow = kt + (32 * ksl + lnx) * (2 * D);
-    const char* vrowp = vt + (32 * ksl + lnx) * (2 * D);
+    int xq = (lnx * G + hg) * (2 * D) + kxx * 16;   // q' and dO rows
+    int xk = (32 * ksl + lnx) * (2 * D) + kxx * 16;  // K and V rows
+    __asm__ volatile("" : "+v"(xq), "+v"(xk));
+    auto rd = [&](const char* buf, int x, int kk) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(buf + (x ^ (32 * kk)));
+    };
+    // operands of k-step kk + 1 are read while the two MFMAs of k-step kk run
+    bf16x8 fq[2], fk[2], fo[2], fv[2];
+    fq[0] = rd(qc, xq, 0);
+    fk[0] = rd(kt, xk, 0);
+    fo[0] = rd(oc, xq, 0);
+    fv[0] = rd(vt, xk, 0);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int off = ((2 * kk) ^ kxx) * 16;
-      sacc = mfma(*reinterpret_cast<const bf16x8*>(qrow + off), *reinterpret_cast<const bf16x8*>(krow + off), sacc);
-      pacc = mfma(*reinterpret_cast<const bf16x8*>(orow + off), *reinterpret_cast<const bf16x8*>(vrowp + off), pacc);
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < D / 16) {
+        fq[nxt] = rd(qc, xq, kk + 1);
+        fk[nxt] = rd(kt, xk, kk + 1);
+        fo[nxt] = rd(oc, xq, kk + 1);
+        fv[nxt] = rd(vt, xk, kk + 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the four DS reads of kk + 1
+      }
+      sacc = mfma(fq[cur], fk[cur], sacc);
+      pacc = mfma(fo[cur], fv[cur], pacc);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then the two MFMAs of kk
     }
     // P = exp2(S') on allowed (row, key) pairs, dZ = P dP'; both to bf16 with rows
     // 16KS .. 16KS + 15 in register order (the A-operand k order). Only steps that need
     // the mask fetch each row's key limit from the lane that loaded it.
+    // (the mask is applied to all 16 elements in one branch: a branch per element split the
+    // step into small blocks the scheduler could not interleave)
     bf16x8 pa[2], za[2];
+    f32x16 pe;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(sacc[r]);
+    if (masked) {
+      // the source lanes from an opaque copy of 4 hi, so that the compiler does not keep 16
+      // loop-invariant lane addresses live across the loop
+      int h4 = 4 * hi;
+      __asm__ volatile("" : "+v"(h4));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int src = 8 * (r >> 2) + h4 + (r & 3);
+        const int lim = __builtin_bit_cast(int, bpermute(src, __builtin_bit_cast(float, mr)));
+        pe[r] = (key < lim && (!HOLE || qrow0 + 32 * s + src < kv)) ? pe[r] : 0.f;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(sacc[r]);
-      if (masked) {
-        const int src = 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int lim = __builtin_bit_cast(int, bpermute(src, __builtin_bit_cast(float, mr)));
-        p = (key < lim && (!HOLE || qrow0 + 32 * s + src < kv)) ? p : 0.f;
-      }
-      pa[r >> 3][r & 7] = static_cast<__bf16>(p);
-      za[r >> 3][r & 7] = static_cast<__bf16>(p * pacc[r]);
+      pa[r >> 3][r & 7] = static_cast<__bf16>(pe[r]);
+      za[r >> 3][r & 7] = static_cast<__bf16>(pe[r] * pacc[r]);
     }
-    // dV += P^T dO, dK += dZ^T Q' (B: dO / q' rows of this head gathered per dims 32mt..)
+    // dV += P^T dO, dK += dZ^T Q' (B: dO / q' rows of this head gathered per dims 32mt..).
+    // Transposing reads: lane t of 16-lane group G16 reads rows 16KS + 8rr + 4(G16 >> 1) + t/4
+    // at chunk (4mt + vcl) ^ swz(row); rows 16KS + r share swz(r), and 4mt + vcl = 4mt ^ vcl,
+    // so the address is the lane's (KS = 0, mt = 0) offset XOR 64 mt, plus KS * 16 G rows.
     const int g16x = lo >> 4, t16x = lo & 15;
     const int vrx = 4 * (g16x >> 1) + (t16x >> 2);
     const int vclx = 2 * (g16x & 1) + ((t16x & 3) >> 1);
     const int vhx = 8 * (t16x & 1);
+    int tl = (vrx * G + hg) * (2 * D) + ((vclx ^ swz<C::CPR>(vrx)) * 16) + vhx;
+    int tu = ((vrx + 8) * G + hg) * (2 * D) + ((vclx ^ swz<C::CPR>(vrx + 8)) * 16) + vhx;
+    __asm__ volatile("" : "+v"(tl), "+v"(tu));
+    // the four transposing reads of (KS, mt) + 1 are issued while the two MFMAs of (KS, mt) run
+    auto trd = [&](int j, bf16x8& dvo, bf16x8& dko) __attribute__((always_inline)) {
+      const int KS = j / (D / 32), mt = j % (D / 32);
+      const int ks = KS * 16 * G * (2 * D);
+      const bf16x4 dol = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(oc + ks + (tl ^ (64 * mt))));
+      const bf16x4 dou = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(oc + ks + (tu ^ (64 * mt))));
+      const bf16x4 qvl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qc + ks + (tl ^ (64 * mt))));
+      const bf16x4 qvu = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qc + ks + (tu ^ (64 * mt))));
+      dvo = __builtin_shufflevector(dol, dou, 0, 1, 2, 3, 4, 5, 6, 7);
+      dko = __builtin_shufflevector(qvl, qvu, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    constexpr int NJ = 2 * (D / 32);
+    bf16x8 bdv[2], bdk[2];
+    trd(0, bdv[0], bdk[0]);
 #pragma unroll
-    for (int KS = 0; KS < 2; ++KS) {
-      const int rl = 16 * KS + vrx, ru = rl + 8;
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const int cl = (((4 * mt + vclx) ^ swz<C::CPR>(rl)) * 16) + vhx;
-        const int cu = (((4 * mt + vclx) ^ swz<C::CPR>(ru)) * 16) + vhx;
-        const char* ol = oc + (rl * G + hg) * (2 * D) + cl;
-        const char* ou = oc + (ru * G + hg) * (2 * D) + cu;
-        const bf16x4 dol = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ol);
-        const bf16x4 dou = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ou);
-        dv[mt] = mfma(pa[KS], __builtin_shufflevector(dol, dou, 0, 1, 2, 3, 4, 5, 6, 7), dv[mt]);
-        const char* ql = qc + (rl * G + hg) * (2 * D) + cl;
-        const char* qu = qc + (ru * G + hg) * (2 * D) + cu;
-        const bf16x4 qvl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ql);
-        const bf16x4 qvu = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)qu);
-        dk[mt] = mfma(za[KS], __builtin_shufflevector(qvl, qvu, 0, 1, 2, 3, 4, 5, 6, 7), dk[mt]);
+    for (int j = 0; j < NJ; ++j) {
+      const int cur = j & 1, nxt = cur ^ 1;
+      if (j + 1 < NJ) {
+        trd(j + 1, bdv[nxt], bdk[nxt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the four reads of j + 1
       }
+      const int KS = j / (D / 32), mt = j % (D / 32);
+      dv[mt] = mfma(pa[KS], bdv[cur], dv[mt]);
+      dk[mt] = mfma(za[KS], bdk[cur], dk[mt]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then the two MFMAs of j
     }
   };
 
