@@ -346,12 +346,15 @@ def backward_leg(w, x, dev, useful_fwd, stream, warmup, steps, nsets):
 
 class ClockSampler:
     """Polls the GPU's current core and memory clocks (MHz) through amdsmi from a thread, about
-    every millisecond, between start() and stop(). Records why when amdsmi is unavailable."""
+    every millisecond, between start() and stop(): the clock-info query and, every tenth poll,
+    the metrics table's per-XCD current gfx clocks (mean over the XCDs). Records why when
+    amdsmi is unavailable."""
 
     def __init__(self, interval_s=0.001):
         import threading
         self.interval = interval_s
-        self.sclk, self.mclk, self.error = [], [], None
+        self.sclk, self.mclk, self.xcd_sclk, self.error = [], [], [], None
+        self.metrics_error = None
         self._stop = threading.Event()
         self._thread = None
         try:
@@ -369,7 +372,16 @@ class ClockSampler:
         m = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.MEM)
         return float(g["clk"]), float(m["clk"])
 
+    def _read_xcds(self):
+        """Mean of the metrics table's per-XCD current gfx clocks (entries amdsmi marks N/A or
+        zero are left out); None when the table has none."""
+        mt = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        v = mt.get("current_gfxclks")
+        vals = [float(x) for x in (v if isinstance(v, (list, tuple)) else [v]) if isinstance(x, (int, float)) and x > 0]
+        return float(np.mean(vals)) if vals else None
+
     def _run(self):
+        k = 0
         while not self._stop.is_set():
             try:
                 g, m = self._read()
@@ -378,6 +390,14 @@ class ClockSampler:
             except Exception as e:  # noqa: BLE001
                 self.error = f"{type(e).__name__}: {e}"
                 return
+            if k % 10 == 0 and self.metrics_error is None:
+                try:
+                    x = self._read_xcds()
+                    if x is not None:
+                        self.xcd_sclk.append(x)
+                except Exception as e:  # noqa: BLE001
+                    self.metrics_error = f"{type(e).__name__}: {e}"
+            k += 1
             time.sleep(self.interval)
 
     def start(self):
@@ -398,7 +418,9 @@ class ClockSampler:
             a = np.array(v)
             return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()), "samples": len(v)}
         return {"source": "amdsmi_get_clock_info (current clock, MHz)", "sclk_mhz": st(self.sclk),
-                "mclk_mhz": st(self.mclk), "error": self.error}
+                "mclk_mhz": st(self.mclk), "error": self.error,
+                "xcd_sclk_mhz": st(self.xcd_sclk), "xcd_source": "amdsmi_get_gpu_metrics_info current_gfxclks (mean over XCDs)",
+                "metrics_error": self.metrics_error}
 
 
 def clock_window(step, sets, stream, useful, seconds=1.0):
@@ -425,10 +447,18 @@ def clock_window(step, sets, stream, useful, seconds=1.0):
     out = sampler.summary()
     out.update({"steps": n, "attn_kernel_ms": {"mean": float(att.mean()), "median": float(np.median(att))},
                 "attn_tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS})
-    if out["sclk_mhz"]:
-        peak = 256 * 4096 * out["sclk_mhz"]["median"] * 1e6 / 1e12
-        out["bf16_peak_at_measured_sclk_tflops"] = peak
-        out["frac_at_measured_sclk"] = tf / peak
+    # the fraction at the measured clock, from the first reading that is plausible: a clock
+    # under which the measured throughput would exceed the dense peak is not the clock the
+    # kernel ran at (some boards report a fixed low level through the clock-info query)
+    for key in ("sclk_mhz", "xcd_sclk_mhz"):
+        if out.get(key):
+            peak = 256 * 4096 * out[key]["median"] * 1e6 / 1e12
+            if tf <= peak:
+                out["clock_used"] = key
+                out["bf16_peak_at_measured_sclk_tflops"] = peak
+                out["frac_at_measured_sclk"] = tf / peak
+                break
+            out.setdefault("implausible", []).append(key)
     return out
 
 

@@ -209,6 +209,15 @@ def test_full_size_sampled_rows(name):
     assert np.array_equal(got[:, 0], np.repeat(v0, w.n_q_heads // w.n_kv_heads, axis=1))
 
 
+def test_hd1024_whole_output():
+    """The 1024^2 HiDream-style workload (batch 2, 1282 tokens, 32 heads) compared with the
+    oracle on every output element, in the launch configuration ha_attn_fwd chooses."""
+    w = W.get_config("hd1024")
+    x = W.generate(w)
+    out, _ = run_fwd(x)
+    compare(f64(out), oracle.hot_path(x), w.dtype, "hd1024 whole output")
+
+
 def test_long_sequence_sampled_rows():
     """A 4096^2 HiDream-style image: 258 causal tokens then a 128 x 128 grid of full rows
     (S = 16642, 261 key tiles per generation row), batch 1, sampled rows against the
