@@ -39,7 +39,9 @@
  *    position check aside). A bad call returns a nonzero ha_status, sets the thread's
  *    ha_last_error() text, and touches neither the device nor the stream. A failed launch
  *    returns HA_ERR_HIP with the HIP error text. No C++ exception crosses this interface.
- *    The library keeps no state between calls apart from that error text.
+ *    The library keeps no state between calls apart from that error text and, for
+ *    ha_attn_fwd_static alone, its per-device scratch array and that array's looked-up
+ *    device address (see there).
  *  - Empty work (batch == 0 or seq_len == 0) is valid and launches nothing.
  */
 #ifndef HA_ATTN_H
