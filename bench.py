@@ -212,6 +212,23 @@ def qkv_leg(w, x, dev, stream, warmup, steps, hidden=4096):
     def prologue():
         B.ha_qk_prologue(desc, pro, q, k, qr, kr, stream=stream)
 
+    # references: one hipBLASLt GEMM against the concatenated weight (all outputs at once),
+    # and a plain device copy of as many bytes as the prologue reads (q and k) and writes,
+    # three buffer pairs cycled as the step cycles its inputs (534 MB: past the 256 MB
+    # Infinity Cache, so the copy runs from and to HBM like the prologue in the step)
+    qkv = torch.empty((T, nq + 2 * nkv), dtype=torch.bfloat16, device="cuda")
+    csrc = [torch.empty(q.numel() + k.numel(), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    cdst = [torch.empty_like(c) for c in csrc]
+    ncopy = [0]
+
+    def concat():
+        torch.matmul(x2, wd.t(), out=qkv)
+
+    def copy():
+        i = ncopy[0] % 3
+        ncopy[0] += 1
+        cdst[i].copy_(csrc[i])
+
     def timed(fn):
         for _ in range(max(1, warmup // 2)):
             fn()
@@ -228,12 +245,19 @@ def qkv_leg(w, x, dev, stream, warmup, steps, hidden=4096):
     fms, n = timed(fused)
     gms, _ = timed(gemms)
     pms, _ = timed(prologue)
+    cms, _ = timed(concat)
+    yms, _ = timed(copy)
     flop = 2.0 * T * hidden * (nq + 2 * nkv)
     tf = flop / (fms / 1e3) / 1e12
+    cbytes = 2 * csrc[0].numel() * csrc[0].element_size()
     return {"tokens": T, "hidden": hidden, "outputs": nq + 2 * nkv, "gflop": flop / 1e9,
             "fused_ms": fms, "fused_tflops": tf, "fused_frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
             "unfused_gemm_ms": gms, "unfused_gemm_tflops": flop / (gms / 1e3) / 1e12,
-            "unfused_prologue_ms": pms, "unfused_total_ms": gms + pms, "calls": n}
+            "unfused_prologue_ms": pms, "unfused_total_ms": gms + pms,
+            "concat_gemm_ms": cms, "concat_gemm_tflops": flop / (cms / 1e3) / 1e12,
+            "copy_ref": {"bytes": cbytes, "ms": yms, "gbps": cbytes / (yms / 1e3) / 1e9,
+                         "what": "torch copy_ of a bf16 tensor the size of q and k together (read + write), 3 buffer pairs cycled"},
+            "calls": n}
 
 
 def training_layout_leg(names, warmup, steps):
@@ -413,10 +437,14 @@ class ClockSampler:
 
     def summary(self):
         def st(v):
+            # "median" is taken over the active samples (at least half the highest reading):
+            # some boards report an idle level for most polls while the kernels run
             if not v:
                 return None
             a = np.array(v)
-            return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()), "samples": len(v)}
+            act = a[a >= 0.5 * a.max()]
+            return {"median": float(np.median(act)), "median_all": float(np.median(a)), "min": float(a.min()),
+                    "max": float(a.max()), "samples": len(v), "active_samples": int(act.size)}
         return {"source": "amdsmi_get_clock_info (current clock, MHz)", "sclk_mhz": st(self.sclk),
                 "mclk_mhz": st(self.mclk), "error": self.error,
                 "xcd_sclk_mhz": st(self.xcd_sclk), "xcd_source": "amdsmi_get_gpu_metrics_info current_gfxclks (mean over XCDs)",

@@ -334,9 +334,14 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
 
   // Masks the tile at position t of S (keys >= lim, and with Gen Images keys whose
   // visibility ends at or before row i) where the tile is partial or runs past the end.
+  // With work items from a table or Gen Images it returns whether the lane's row sees a key
+  // of the tile (a part of a split block can hold tiles that some of its rows cannot see
+  // yet, and a tile list can start with tiles hidden from some rows).
+  constexpr bool TRACK = ITEMS || KVIS;
   auto mask = [&](f32x16 (&sc)[2], int t) {
     const int tile = tile_at(t);
-    if (t < kfull && (tile + 1) * BK <= S) return;
+    if (t < kfull && (tile + 1) * BK <= S) return true;
+    bool any = false;
     if constexpr (KVIS) {
       // the lane's keys come in runs of 4: key_vis rows are padded, so every run is in bounds
       const int* kv = a.key_vis + (int64_t)b * a.kv_stride + tile * BK + 4 * hi;
@@ -349,9 +354,15 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
             const int key = tile * BK + 32 * kt + 8 * q4 + 4 * hi + e;
-            sc[kt][r] = (key >= lim || i >= vis[e]) ? -INFINITY : sc[kt][r];
+            const bool hide = key >= lim || i >= vis[e];
+            if constexpr (TRACK) any = any || !hide;
+            sc[kt][r] = hide ? -INFINITY : sc[kt][r];
           }
         }
+      if constexpr (TRACK) {  // the row's other 32 keys sit in the partner lane (lane ^ 32)
+        const auto r = __builtin_amdgcn_permlane32_swap((unsigned)any, (unsigned)any, false, false);
+        any = (r[0] | r[1]) != 0;
+      }
     } else {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -360,7 +371,9 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
           const int key = tile * BK + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
           sc[kt][r] = key >= lim ? -INFINITY : sc[kt][r];
         }
+      any = lim > tile * BK;  // the tile's keys are contiguous from tile * BK
     }
+    return any;
   };
 
   // O^T += V^T P^T for one tile; the A operand of K step KS, dims 32mt.. comes from two
@@ -384,6 +397,7 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // t-1 .. t+2 present, tiles t .. t+2 full and inside the sequence) have no branch at
   // all, so the two MFMA chains and the exponentials interleave freely.
   bool off_range = false;
+  bool seen = false;  // (table work items, Gen Images) the row has seen a key of its walk
   auto step = [&](auto fast_tag, auto par_tag, int t, f32x16 (&sc)[2], f32x16 (&sn)[2],
                   bf16x8 (&pfp)[4], bf16x8 (&pf)[4]) {
     constexpr bool FAST = decltype(fast_tag)::value;
@@ -405,9 +419,16 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
       sn[1] = s1[1];
     }
     if (FAST || t >= 1) pv(vr, pfp);
-    if (!FAST) mask(sc, t);
+    bool vis = true;
+    if (!FAST) vis = mask(sc, t);
     const float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
-    off_range = off_range || !(ts <= kHi) || !(l + ts >= kLo);
+    if constexpr (TRACK) {
+      // a row that has seen no key of its part yet has nothing to be out of range
+      seen = seen || vis;
+      off_range = off_range || !(ts <= kHi) || (seen && !(l + ts >= kLo));
+    } else {
+      off_range = off_range || !(ts <= kHi) || !(l + ts >= kLo);
+    }
     l += ts;
     // read past the barrier, at the end of the step: no wave publishes again before the
     // next odd step's barrier, which every wave reaches only after this read

@@ -320,19 +320,22 @@ __global__ __launch_bounds__((CfgP<WN, WM, MT, BK, NST>::NT), 1) void qkv_kernel
 }
 
 // The kernel's configurations: 2 heads x 256 tokens per workgroup (8 waves of 128 features x
-// 64 tokens), and for the tail 2 heads x 128 tokens (8 waves of 128 x 32); K in stages of 32
-// in a ring of 5 (160 KB of LDS: three stages in flight behind the one computed).
+// 64 tokens), and for the tail 1 head x 128 tokens (4 waves of 128 x 32, a quarter of a main
+// tile, so the tail's tiles spread over about as many CUs as a round has); K in stages of
+// 32 in a ring of 5 (160 KB of LDS for the main tile, 80 KB for the tail's: three stages in
+// flight behind the one computed).
 constexpr int kWN = 2, kWM = 4, kBK = 32, kNST = 5;
+constexpr int kTailWN = 1, kTailWM = 4, kTailMT = 1;
 using Main = CfgP<kWN, kWM, 2, kBK, kNST>;
-using Tail = CfgP<kWN, kWM, 1, kBK, kNST>;
 
-template <typename C, int MT>
+template <int WN, int WM, int MT>
 hipError_t launch_part(const QkvArgs& a, hipStream_t stream) {
+  using C = CfgP<WN, WM, MT, kBK, kNST>;
   const int nM = (a.T - a.m_begin + C::BM - 1) / C::BM;
-  const int nN = (a.Hq + 2 * a.Hkv + kWN - 1) / kWN;
+  const int nN = (a.Hq + 2 * a.Hkv + WN - 1) / WN;
   const int total = nM * nN;
   const int grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((qkv_kernel<kWN, kWM, MT, kBK, kNST>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((qkv_kernel<WN, WM, MT, kBK, kNST>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -342,7 +345,7 @@ int qkv_block_tokens() { return Main::BM; }
 
 // One workgroup runs per CU at a time. The 256-token tiles take the tokens that fill whole
 // rounds of the CUs; the tokens left over (which would run a last, mostly idle round) go to
-// half-height tiles, twice as many and each half as long.
+// tiles of one head and 128 tokens, four times as many and each a quarter as long.
 hipError_t launch_qkv(const QkvArgs& a, int n_cus, hipStream_t stream) {
   const int nN = (a.Hq + 2 * a.Hkv + kWN - 1) / kWN;
   const int full = a.T / Main::BM;                         // whole 256-token tiles
@@ -352,13 +355,13 @@ hipError_t launch_qkv(const QkvArgs& a, int n_cus, hipStream_t stream) {
   if (m_main > 0) {
     p.m_begin = 0;
     p.T = m_main * Main::BM;
-    const hipError_t e = launch_part<Main, 2>(p, stream);
+    const hipError_t e = launch_part<kWN, kWM, 2>(p, stream);
     if (e != hipSuccess) return e;
   }
   if (m_main * Main::BM < a.T) {
     p = a;
     p.m_begin = m_main * Main::BM;
-    return launch_part<Tail, 1>(p, stream);
+    return launch_part<kTailWN, kTailWM, kTailMT>(p, stream);
   }
   return hipSuccess;
 }
