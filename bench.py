@@ -504,7 +504,8 @@ def _timed_calls(fn, stream, n):
 
 def configs_leg(names, warmup, steps):
     """Every workload shape besides the headline: the whole ha_attn_fwd call (classifier,
-    split plan where the planner takes one, prologue, attention, merge) and, for layouts the
+    split plan where the planner takes one, prologue, attention, merge), eager and replayed
+    from a HIP graph, and, for layouts the
     planned path takes (no Gen Images), the attention kernel alone (ha_attn_fwd_planned after
     one classifier and prologue call). HIP events around each call on the launch stream;
     input sets cycled so that together they exceed the 256 MB Infinity Cache."""
@@ -559,6 +560,23 @@ def configs_leg(names, warmup, steps):
              "split_plan": nbytes > B.ha_attn_workspace_bytes(
                  B.AttnDesc(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, x.segments,
                             split_parts=1), pro)}
+        # the same call captured in a HIP graph per input set, replayed: the launch gaps go
+        graphs = []
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                B.ha_attn_fwd(desc, pro, s["q"], s["k"], s["v"], s["out"], s["ws"])
+            graphs.append(g)
+
+        def replay(i):
+            graphs[i % nsets].replay()
+
+        for i in range(max(2, warmup)):
+            replay(i)
+        gm = _timed_calls(replay, stream, n)
+        r.update({"fwd_graph_ms": {"mean": float(gm.mean()), "median": float(np.median(gm))},
+                  "fwd_graph_tflops": useful / (float(np.median(gm)) / 1e3) / 1e12})
+        del graphs
         if not any(int(k) == 3 for k in x.segments[..., 2].ravel()):
             for s in sets:
                 B.ha_classify_tiles(pdesc, None, s["ranges"], s["lim"], stream)

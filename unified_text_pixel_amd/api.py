@@ -61,6 +61,24 @@ class HybridAttention:
         B.ha_attn_fwd(self.desc, self.pro, q, k, v, out, self.workspace, stream=stream)
         return out
 
+    def graphed(self, q, k, v):
+        """(replay, out): one forward on these q, k, v buffers captured in a HIP graph.
+        replay() reruns the whole call (classifier, split plan, prologue, attention, merge)
+        on the buffers' current contents with one graph launch on the current stream, writing
+        out. The library allocates nothing, synchronises nothing and records no memory sets
+        inside ha_attn_fwd, so the graph replays what was captured; its launches use this
+        object's workspace, so replays and eager calls of one object must not overlap."""
+        out = torch.empty(self.shape, dtype=q.dtype, device=q.device)
+        side = torch.cuda.Stream(device=q.device)  # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self(q, k, v, out)  # outside the capture: the library's one-time device queries
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self(q, k, v, out)
+        return graph.replay, out
+
     # ---- training (bf16, Hq / Hkv in {1, 2, 4})
     def forward_train(self, q, k, v, stream=None):
         """(out, lse): the forward plus each row's log-sum-exp [B][Hq][S] for backward()."""
