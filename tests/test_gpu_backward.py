@@ -26,7 +26,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import desc_for, f64, prologue_for, require_gpu
+from gpu_helpers import desc_for, f64, plan, prologue_for, require_gpu
 from unified_text_pixel_amd import binding as B
 from workloads.device import to_device
 
@@ -146,6 +146,26 @@ def test_backward_small_layouts(name):
     masks = [oracle.explicit_mask(x.segments[b], w.seq_len) for b in range(w.batch)]
     q_rot, k_rot = oracle.prologue(x)
     check_lse(got["lse"], oracle.attention_lse(q_rot, k_rot, masks))
+    want = oracle.path_backward(x, dout)
+    for t in ("dq", "dk", "dv"):
+        check(f"{name} {t}", got[t], want[t])
+    if w.qk_norm:
+        for t in ("dw_q", "dw_k"):
+            check(f"{name} {t}", got[t], want[t])
+
+
+@pytest.mark.parametrize("name", ["hd_small", "gca_small", "d64", "gen_small", "gen_long"])
+def test_backward_two_heads_per_step(name):
+    """G = 4 with dK/dV in two launches: two heads per step over 128-key blocks for the
+    keys whose blocks fill two whole rounds of the CUs, four heads per step over 64-key blocks
+    for the rest (gen_long: no rest). plan_cus = 2 gives these small layouts that split."""
+    w = SMALL[name]
+    assert w.n_q_heads // w.n_kv_heads == 4
+    print(f"case {name}: S={w.seq_len} plan_cus 2", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w, seed=79)
+    with plan(plan_cus=2):
+        got = run_train(x, dout)
     want = oracle.path_backward(x, dout)
     for t in ("dq", "dk", "dv"):
         check(f"{name} {t}", got[t], want[t])

@@ -11,15 +11,16 @@
 // P_ij = exp(Z_ij - lse_i); q comes in as q' = scale log2(e) q (the prologue's prescaled
 // output), so q' . k is Z in log2 units and P = exp2(q' . k - log2(e) lse).
 //
-// bwd_dkdv: one workgroup per (batch, KV head, block of 256/G keys). Wave w serves query
-//   head g*G + w%G and keys 32*(w/G) .. +32 of the block. Per step of 32 query rows the
-//   q' and dO rows of all G heads are copied into LDS (global_load_lds, double-buffered).
-//   In the orientation S = Q' K^T (v_mfma_f32_32x32x16_bf16, A = q' rows, B = K^T, both
-//   from LDS) a lane holds one key and 16 of the 32 rows, so P and dZ rounded to bf16 are
-//   already the A operand of dV += P^T dO and dK += dZ^T Q', whose B operands are the dO
-//   and q' rows gathered in the same row order by ds_read_b64_tr_b16. A row's lse, delta
-//   and limit come from the lane that loaded them (ds_bpermute). At the end the G heads'
-//   partial sums meet in LDS.
+// bwd_dkdv: one workgroup per (batch, KV head, block of 256/HPS keys), HPS heads per step
+//   (HPS = G, or 2 of G = 4 on large shapes). Wave w serves head slot w%HPS and keys
+//   32*(w/HPS) .. +32 of the block. Per step of 32 query rows and HPS heads (the G/HPS head
+//   groups of a row block in turn) the q' and dO rows are copied into LDS (global_load_lds,
+//   double-buffered). In the orientation S = Q' K^T (v_mfma_f32_32x32x16_bf16, A = q'
+//   rows, B = K^T, both from LDS) a lane holds one key and 16 of the 32 rows, so P and dZ
+//   rounded to bf16 are already the A operand of dV += P^T dO and dK += dZ^T Q', whose B
+//   operands are the dO and q' rows gathered in the same row order by ds_read_b64_tr_b16.
+//   A row's lse, delta and limit come from the lane that loaded them (ds_bpermute). At the
+//   end the HPS head slots' partial sums meet in LDS.
 // bwd_dq: the forward's shape: one workgroup per (batch, KV head, query block), one lane
 //   per query row. Per 64-key tile S^T = K Q'^T and dP^T = V dO^T (A from LDS, B = the
 //   row's q' and dO held in registers); dZ^T, rounded to bf16, is the B operand of
@@ -146,24 +147,25 @@ __global__ __launch_bounds__(256) void bwd_delta(const __bf16* out, const __bf16
 }
 
 // ====================================================================== dK, dV
-template <int D, int G>
+template <int D, int G, int HPS>
 struct CfgKV {
-  static constexpr int NS = 8 / G;                // 32-key slices per work item
+  static constexpr int NS = 8 / HPS;              // 32-key slices per work item
   static constexpr int KB = 32 * NS;              // keys per work item
   static constexpr int CPR = D / 8;               // 16-byte chunks per head row
-  static constexpr int QROWB = G * D * 2;         // one step row: the G heads' q' (or dO)
+  static constexpr int QROWB = HPS * D * 2;       // one step row: HPS heads' q' (or dO)
   static constexpr int QBYTES = 32 * QROWB;       // one step tile (32 rows)
   static constexpr int KVBYTES = KB * D * 2;      // the item's K (or V) rows
   static constexpr int SUB = 8 / G;               // 32-row steps per query block
+  static constexpr int NHP = G / HPS;             // steps (head groups) per 32 rows
 };
 
 // HOLE: a layout with Gen Images. Each lane's key carries its visibility (the rows below
 // it see the key), and the block's smallest and largest visibility bound the steps: rows
 // at or after the largest see none of the block's keys, rows at or after the smallest need
 // the per-pair mask.
-template <int D, int G, bool HOLE>
+template <int D, int G, bool HOLE, int HPS>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
-  using C = CfgKV<D, G>;
+  using C = CfgKV<D, G, HPS>;
   __shared__ __attribute__((aligned(1024))) char kt[C::KVBYTES];
   __shared__ __attribute__((aligned(1024))) char vt[C::KVBYTES];
   __shared__ __attribute__((aligned(1024))) char q0[C::QBYTES];
@@ -174,13 +176,13 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   const int S = a.S, nq = a.nq;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wave % G, ksl = wave / G;
+  const int hs = wave % HPS, ksl = wave / HPS;  // head slot of a step, 32-key slice
   const int hi = lane >> 5, ln = lane & 31;
-  const int nkb = (S + C::KB - 1) / C::KB;
+  const int nkb = (a.k_end - a.k_begin + C::KB - 1) / C::KB;
   int bg, kbk;
   pair_slot(blockIdx.x, a.B * a.Hkv, nkb, &bg, &kbk);
-  const int b = bg / a.Hkv, g = bg % a.Hkv, h = g * G + hg;
-  const int k0 = kbk * C::KB;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int k0 = a.k_begin + kbk * C::KB;
   const int key = k0 + 32 * ksl + ln;  // this lane's key (lanes l and l + 32 share it)
   const int BQ = 32 * C::SUB;          // rows of a forward query block
   const int qrow0 = S - nq * BQ;       // first row of query block 0 (end-aligned blocks)
@@ -239,8 +241,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   const int64_t qstride = (int64_t)a.Hq * D * 2;
   const char* qbase = static_cast<const char*>(a.q) + ((int64_t)b * S * a.Hq + g * G) * D * 2;
   const char* obase = static_cast<const char*>(a.dout) + ((int64_t)b * S * a.Hq + g * G) * D * 2;
-  const float* lse_h = a.lse + ((int64_t)b * a.Hq + h) * S;
-  const float* del_h = a.delta + ((int64_t)b * a.Hq + h) * S;
   const int32_t* lim_b = a.row_limit + (int64_t)b * S;
   // step s into a tile pair; the lane's row (ln) values into registers: log2(e) lse,
   // delta and the row's key limit (0 for rows before the sequence, which see no key)
@@ -248,14 +248,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   qd_dma.init(lane);
   // raw loads only: using a loaded value before the step's DMA has landed would make the
   // compiler wait for that DMA (vector memory operations complete in order)
-  auto fetch = [&](int s, char* qd, char* od, float& lr, float& dr, int& mr) __attribute__((always_inline)) {
+  // substep u = (32-row step s, head group hp): the rows of heads g G + hp HPS .. + HPS
+  auto fetch = [&](int u, char* qd, char* od, float& lr, float& dr, int& mr) __attribute__((always_inline)) {
+    const int s = u / C::NHP, hp = u % C::NHP;
     const int r0 = qrow0 + 32 * s;
     const int ic = max(r0 + ln, 0);
-    lr = lse_h[ic];
-    dr = del_h[ic];
+    const int64_t hrow = ((int64_t)b * a.Hq + g * G + hp * HPS + hs) * S;
+    lr = a.lse[hrow + ic];
+    dr = a.delta[hrow + ic];
     mr = lim_b[ic];
-    qd_dma.issue(qbase, qstride, r0, S - 1, qd, wave);
-    qd_dma.issue(obase, qstride, r0, S - 1, od, wave);
+    qd_dma.issue(qbase + hp * HPS * D * 2, qstride, r0, S - 1, qd, wave);
+    qd_dma.issue(obase + hp * HPS * D * 2, qstride, r0, S - 1, od, wave);
+  };
+  auto next_sub = [&](int u) __attribute__((always_inline)) {
+    if (u % C::NHP + 1 < C::NHP) return u + 1;
+    const int s2 = next_step(u / C::NHP);
+    return s2 < 0 ? -1 : s2 * C::NHP;
   };
   // a step needs the per-pair mask unless every row of it is inside the sequence and
   // attends every key of the block (keys [0, 64 kfull) of its query block, and < S)
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
     f32x16 sacc = mfma(split_col(lr * kLog2e), ones, f32x16{});
     f32x16 pacc = mfma(split_col(dr), ones, f32x16{});
     if (qrow0 + 32 * s + ln < 0) mr = 0;  // rows before the sequence see no key
-    int xq = (lnx * G + hg) * (2 * D) + kxx * 16;   // q' and dO rows
+    int xq = (lnx * HPS + hs) * (2 * D) + kxx * 16;   // q' and dO rows
     int xk = (32 * ksl + lnx) * (2 * D) + kxx * 16;  // K and V rows
     __asm__ volatile("" : "+v"(xq), "+v"(xk));
     auto rd = [&](const char* buf, int x, int kk) __attribute__((always_inline)) {
@@ -365,13 +373,13 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
     const int vrx = 4 * (g16x >> 1) + (t16x >> 2);
     const int vclx = 2 * (g16x & 1) + ((t16x & 3) >> 1);
     const int vhx = 8 * (t16x & 1);
-    int tl = (vrx * G + hg) * (2 * D) + ((vclx ^ swz<C::CPR>(vrx)) * 16) + vhx;
-    int tu = ((vrx + 8) * G + hg) * (2 * D) + ((vclx ^ swz<C::CPR>(vrx + 8)) * 16) + vhx;
+    int tl = (vrx * HPS + hs) * (2 * D) + ((vclx ^ swz<C::CPR>(vrx)) * 16) + vhx;
+    int tu = ((vrx + 8) * HPS + hs) * (2 * D) + ((vclx ^ swz<C::CPR>(vrx + 8)) * 16) + vhx;
     __asm__ volatile("" : "+v"(tl), "+v"(tu));
     // the four transposing reads of (KS, mt) + 1 are issued while the two MFMAs of (KS, mt) run
     auto trd = [&](int j, bf16x8& dvo, bf16x8& dko) __attribute__((always_inline)) {
       const int KS = j / (D / 32), mt = j % (D / 32);
-      const int ks = KS * 16 * G * (2 * D);
+      const int ks = KS * 16 * HPS * (2 * D);
       const bf16x4 dol = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(oc + ks + (tl ^ (64 * mt))));
       const bf16x4 dou = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(oc + ks + (tu ^ (64 * mt))));
       const bf16x4 qvl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qc + ks + (tl ^ (64 * mt))));
@@ -400,24 +408,25 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   // tiles (wait + barrier, which also retires every wave's reads of the pair it refills)
   float la = 0.f, da = 0.f, lb = 0.f, db = 0.f;
   int ma = 0, mb = 0;
-  int s = next_step(-1);
-  if (s >= 0) fetch(s, q0, o0, la, da, ma);
-  while (s >= 0) {
+  const int s_first = next_step(-1);
+  int u = s_first < 0 ? -1 : s_first * C::NHP;
+  if (u >= 0) fetch(u, q0, o0, la, da, ma);
+  while (u >= 0) {
     // the step's mask flag is read before the wait, so using it waits for nothing issued later
-    const int s1 = next_step(s);
-    const bool m0 = masked_step(s);
+    const int u1 = next_sub(u);
+    const bool m0 = masked_step(u / C::NHP);
     wait_vm();
     __syncthreads();
-    if (s1 >= 0) fetch(s1, q1, o1, lb, db, mb);
-    compute(q0, o0, la, da, ma, s, m0);
-    if (s1 < 0) break;
-    const int s2 = next_step(s1);
-    const bool m1 = masked_step(s1);
+    if (u1 >= 0) fetch(u1, q1, o1, lb, db, mb);
+    compute(q0, o0, la, da, ma, u / C::NHP, m0);
+    if (u1 < 0) break;
+    const int u2 = next_sub(u1);
+    const bool m1 = masked_step(u1 / C::NHP);
     wait_vm();
     __syncthreads();
-    if (s2 >= 0) fetch(s2, q0, o0, la, da, ma);
-    compute(q1, o1, lb, db, mb, s1, m1);
-    s = s2;
+    if (u2 >= 0) fetch(u2, q0, o0, la, da, ma);
+    compute(q1, o1, lb, db, mb, u1 / C::NHP, m1);
+    u = u2;
   }
   wait_vm();  // K/V DMA of an item with no step
 
@@ -425,8 +434,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dk[mt] *= kLn2;
 
-  // sum the G heads' partials (waves ksl*G .. +G) through LDS, 8 registers per lane per
-  // round; wave hg == 0 of each slice stores. Element (r, lane) of dv[mt] / dk[mt] is key
+  // sum the HPS head slots' partials (waves ksl*HPS .. +HPS) through LDS, 8 registers per
+  // lane per round; wave hs == 0 of each slice stores. Element (r, lane) of dv[mt] / dk[mt] is key
   // k0 + 32 ksl + 8(r/4) + 4hi + r%4, dim 32 mt + ln.
   float* red = reinterpret_cast<float*>(C::QBYTES >= 16384 ? q0 : kt);
   __bf16* dvo = static_cast<__bf16*>(a.dv) + ((int64_t)b * S * a.Hkv + g) * D;
@@ -454,15 +463,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = acc[8 * half + e];
-        if constexpr (G > 1) {
+        if constexpr (HPS > 1) {
           __syncthreads();  // the previous round's (or the last step's) reads are done
           f32x4* w = reinterpret_cast<f32x4*>(red + (wave * 64 + lane) * 8);
           w[0] = f32x4{x[0], x[1], x[2], x[3]};
           w[1] = f32x4{x[4], x[5], x[6], x[7]};
           __syncthreads();
-          if (hg == 0) {
+          if (hs == 0) {
 #pragma unroll
-            for (int o = 1; o < G; ++o) {
+            for (int o = 1; o < HPS; ++o) {
               const f32x4* rd = reinterpret_cast<const f32x4*>(red + ((wave + o) * 64 + lane) * 8);
               const f32x4 u = rd[0], v = rd[1];
 #pragma unroll
@@ -641,15 +650,38 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
 }
 
 // ====================================================================== launch
-template <int D, int G>
-hipError_t launch_kv(const BwdArgs& a, hipStream_t stream) {
-  const int64_t nkb = (a.S + CfgKV<D, G>::KB - 1) / CfgKV<D, G>::KB;
+// keys [k_begin, k_end) in blocks of CfgKV<D, G, HPS>::KB
+template <int D, int G, int HPS>
+hipError_t launch_kv(BwdArgs a, int k_begin, int k_end, hipStream_t stream) {
+  using C = CfgKV<D, G, HPS>;
+  a.k_begin = k_begin;
+  a.k_end = k_end;
+  const int64_t nkb = (k_end - k_begin + C::KB - 1) / C::KB;
   const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * nkb));
   if (a.key_vis)
-    hipLaunchKernelGGL((bwd_dkdv<D, G, true>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv<D, G, true, HPS>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv<D, G, false>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv<D, G, false, HPS>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
+}
+
+// G = 4: two heads per step over 128-key blocks (half the q' and dO bytes per MFMA of all
+// four heads per step over 64-key blocks) for the keys whose blocks fill at least two whole
+// rounds of the CUs; the remaining keys in 64-key blocks, so that the last round is not
+// mostly idle. Shapes whose 128-key blocks fill fewer rounds keep 64-key blocks throughout
+// (four times as many small blocks balance the CUs better there).
+template <int D>
+hipError_t launch_kv_g4(const BwdArgs& a, hipStream_t stream) {
+  constexpr int KB2 = CfgKV<D, 4, 2>::KB;
+  const int64_t pairs = (int64_t)a.B * a.Hkv;
+  const int64_t rounds = a.n_cus > 0 ? pairs * (a.S / KB2) / a.n_cus : 0;
+  const int k_main = rounds >= 2 ? (int)(rounds * a.n_cus / pairs * KB2) : 0;
+  if (k_main > 0) {
+    const hipError_t e = launch_kv<D, 4, 2>(a, 0, k_main, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (k_main < a.S) return launch_kv<D, 4, 4>(a, k_main, a.S, stream);
+  return hipSuccess;
 }
 
 template <int D, int G>
@@ -681,8 +713,9 @@ hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  if (a.D == 128) return G == 1 ? launch_kv<128, 1>(a, stream) : G == 2 ? launch_kv<128, 2>(a, stream) : launch_kv<128, 4>(a, stream);
-  return G == 1 ? launch_kv<64, 1>(a, stream) : G == 2 ? launch_kv<64, 2>(a, stream) : launch_kv<64, 4>(a, stream);
+  if (a.D == 128)
+    return G == 1 ? launch_kv<128, 1, 1>(a, 0, a.S, stream) : G == 2 ? launch_kv<128, 2, 2>(a, 0, a.S, stream) : launch_kv_g4<128>(a, stream);
+  return G == 1 ? launch_kv<64, 1, 1>(a, 0, a.S, stream) : G == 2 ? launch_kv<64, 2, 2>(a, 0, a.S, stream) : launch_kv_g4<64>(a, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {

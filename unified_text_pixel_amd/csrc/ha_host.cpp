@@ -1036,6 +1036,7 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   a.tile_count = hole.tile_count;
   a.kv_stride = ha::key_vis_stride(S);
   a.nk = nk;
+  a.n_cus = plan_cus(desc);
   if ((st = check_launch(ha::launch_bwd_dkdv(a, s), s, "backward dK dV")) != HA_OK) return st;
   if ((st = check_launch(ha::launch_bwd_dq(a, s), s, "backward dQ")) != HA_OK) return st;
   // through the rotary embedding and RMSNorm to the inputs

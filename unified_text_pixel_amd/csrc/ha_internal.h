@@ -183,6 +183,9 @@ struct BwdArgs {
   const int32_t* tiles;
   const int32_t* tile_count;
   int32_t kv_stride, nk;
+  int32_t n_cus;             // CUs the dK/dV launches are shaped for (0: unknown)
+  // the dK/dV kernel's key range [k_begin, k_end) of one launch (set by launch_bwd_dkdv)
+  int32_t k_begin, k_end;
 };
 hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int B, int S, int Hq, int D,
                             hipStream_t stream);
