@@ -98,8 +98,9 @@ typedef struct {
   int32_t split_parts;      /* split plan of the bf16 forward (see ha_attn_fwd): 0 lets the
                                planner decide, 1 never splits, P in [2, 64] splits every
                                query block into P parts */
-  int32_t plan_cus;         /* CUs the planner balances the work items over: 0 means the
-                               current device's count, n > 0 plans for n CUs */
+  int32_t plan_cus;         /* CUs the work is balanced over (the forward's split plan,
+                               the backward's dK/dV launches): 0 means the current
+                               device's count, n > 0 plans for n CUs */
 } ha_attn_desc;
 
 /* q/k prologue: RMSNorm over head_dim (y = x / sqrt(mean(x^2) + eps) * w, before the

@@ -174,6 +174,23 @@ def test_backward_two_heads_per_step(name):
             check(f"{name} {t}", got[t], want[t])
 
 
+@pytest.mark.parametrize("kind", [F, GEN])
+def test_backward_tail_in_parts(kind):
+    """With 4 CUs planned, 1054 keys of one KV head: keys [0, 1024) in 128-key blocks (two
+    rounds of 4), the last 30 keys in one 64-key block whose 32-row steps are cut into 4
+    ranges, each writing fp32 partial dK and dV that are summed in part order."""
+    w = small([W.Segment(C, 30), W.Segment(kind, 1024, (32, 32))], hq=4, hkv=1, batch=1,
+              rope="2d", theta=1e4)
+    print(f"case tail in parts: kind {kind} S={w.seq_len} plan_cus 4", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w, seed=80)
+    with plan(plan_cus=4):
+        got = run_train(x, dout)
+    want = oracle.path_backward(x, dout)
+    for t in ("dq", "dk", "dv", "dw_q", "dw_k"):
+        check(f"tail in parts {t}", got[t], want[t])
+
+
 def test_backward_hd1024_full():
     """The 1024^2 HiDream layout at full size (both batch items, every head)."""
     w = W.get_config("hd1024")

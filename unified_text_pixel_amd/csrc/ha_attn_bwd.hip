@@ -29,6 +29,7 @@
 //
 // LDS tiles are row-major with 16-byte chunks XOR-swizzled by swz(row) (below); a step
 // tile of q' or dO keeps the G heads of one row side by side.
+#include <algorithm>
 #include <type_traits>
 
 #include "ha_internal.h"
@@ -179,8 +180,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   const int hs = wave % HPS, ksl = wave / HPS;  // head slot of a step, 32-key slice
   const int hi = lane >> 5, ln = lane & 31;
   const int nkb = (a.k_end - a.k_begin + C::KB - 1) / C::KB;
-  int bg, kbk;
-  pair_slot(blockIdx.x, a.B * a.Hkv, nkb, &bg, &kbk);
+  int bg, slot;
+  pair_slot(blockIdx.x, a.B * a.Hkv, nkb * a.n_parts, &bg, &slot);
+  const int kbk = slot / a.n_parts, part = slot % a.n_parts;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int k0 = a.k_begin + kbk * C::KB;
   const int key = k0 + 32 * ksl + ln;  // this lane's key (lanes l and l + 32 share it)
@@ -226,7 +228,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
 
   // step s = 32 rows starting at qrow0 + 32 s; active when its query block attends a key
   // >= k0 (then it attends k0: rows see prefixes) and some row is >= 0
-  const int nsteps = nq * C::SUB;
+  // this workgroup's part of the 32-row steps: [s_lo, s_hi)
+  const int nsteps_all = nq * C::SUB;
+  const int s_lo = (int)((int64_t)part * nsteps_all / a.n_parts);
+  const int nsteps = (int)((int64_t)(part + 1) * nsteps_all / a.n_parts);
   auto next_step = [&](int s) __attribute__((always_inline)) {
     for (++s; s < nsteps; ++s) {
       if (qrow0 + 32 * s + 31 < 0) continue;
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   // tiles (wait + barrier, which also retires every wave's reads of the pair it refills)
   float la = 0.f, da = 0.f, lb = 0.f, db = 0.f;
   int ma = 0, mb = 0;
-  const int s_first = next_step(-1);
+  const int s_first = next_step(s_lo - 1);
   int u = s_first < 0 ? -1 : s_first * C::NHP;
   if (u >= 0) fetch(u, q0, o0, la, da, ma);
   while (u >= 0) {
@@ -440,12 +445,21 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdArgs a) {
   float* red = reinterpret_cast<float*>(C::QBYTES >= 16384 ? q0 : kt);
   __bf16* dvo = static_cast<__bf16*>(a.dv) + ((int64_t)b * S * a.Hkv + g) * D;
   float* dko = a.dk + ((int64_t)b * S * a.Hkv + g) * D;
+  // a part of the steps writes fp32 partial sums to its slot, keys relative to k_begin
+  const int nkeys = a.k_end - a.k_begin;
+  float* pdv = a.part_dv ? a.part_dv + (((int64_t)part * a.B + b) * nkeys * a.Hkv + g) * D : nullptr;
+  float* pdk = a.part_dk ? a.part_dk + (((int64_t)part * a.B + b) * nkeys * a.Hkv + g) * D : nullptr;
   auto emit = [&](int which, int mt, int half, const float (&x)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int r = 8 * half + e;
       const int kj = k0 + 32 * ksl + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (kj >= S) continue;
+      if (kj >= a.k_end) continue;
+      if (pdv) {
+        const int64_t at = (int64_t)(kj - a.k_begin) * a.Hkv * D + 32 * mt + ln;
+        (which == 0 ? pdv : pdk)[at] = x[e];
+        continue;
+      }
       const int64_t at = (int64_t)kj * a.Hkv * D + 32 * mt + ln;
       if (which == 0)
         dvo[at] = static_cast<__bf16>(x[e]);
@@ -650,14 +664,17 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
 }
 
 // ====================================================================== launch
-// keys [k_begin, k_end) in blocks of CfgKV<D, G, HPS>::KB
+// keys [k_begin, k_end) in blocks of CfgKV<D, G, HPS>::KB, each block's steps in n_parts
+// ranges (n_parts > 1: partial sums to a.part_dk / a.part_dv)
 template <int D, int G, int HPS>
-hipError_t launch_kv(BwdArgs a, int k_begin, int k_end, hipStream_t stream) {
+hipError_t launch_kv(BwdArgs a, int k_begin, int k_end, int n_parts, hipStream_t stream) {
   using C = CfgKV<D, G, HPS>;
   a.k_begin = k_begin;
   a.k_end = k_end;
+  a.n_parts = n_parts;
+  if (n_parts == 1) a.part_dk = a.part_dv = nullptr;
   const int64_t nkb = (k_end - k_begin + C::KB - 1) / C::KB;
-  const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * nkb));
+  const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * nkb * n_parts));
   if (a.key_vis)
     hipLaunchKernelGGL((bwd_dkdv<D, G, true, HPS>), grid, dim3(512), 0, stream, a);
   else
@@ -665,23 +682,41 @@ hipError_t launch_kv(BwdArgs a, int k_begin, int k_end, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// G = 4: two heads per step over 128-key blocks (half the q' and dO bytes per MFMA of all
-// four heads per step over 64-key blocks) for the keys whose blocks fill at least two whole
-// rounds of the CUs; the remaining keys in 64-key blocks, so that the last round is not
-// mostly idle. Shapes whose 128-key blocks fill fewer rounds keep 64-key blocks throughout
-// (four times as many small blocks balance the CUs better there).
+// sums the tail's partial dK and dV over the parts in part order: dk (fp32) and dv (bf16)
+// of keys [k_main, S)
+__global__ __launch_bounds__(256) void kv_part_sum_kernel(const float* part_dk, const float* part_dv, int parts,
+                                                          int64_t n, int64_t per_item, int64_t item_stride,
+                                                          int64_t item_off, float* dk, __bf16* dv) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float sk = 0.f, sv = 0.f;
+  for (int p = 0; p < parts; ++p) {
+    sk += part_dk[p * n + i];
+    sv += part_dv[p * n + i];
+  }
+  const int64_t b = i / per_item, r = i % per_item;
+  const int64_t at = b * item_stride + item_off + r;
+  dk[at] = sk;
+  dv[at] = static_cast<__bf16>(sv);
+}
+
+// G = 4 (see BwdArgs): the two-heads-per-step launch for keys [0, k_main), then the rest in
+// 64-key blocks, their steps in tail_parts ranges when few blocks are left
 template <int D>
 hipError_t launch_kv_g4(const BwdArgs& a, hipStream_t stream) {
-  constexpr int KB2 = CfgKV<D, 4, 2>::KB;
-  const int64_t pairs = (int64_t)a.B * a.Hkv;
-  const int64_t rounds = a.n_cus > 0 ? pairs * (a.S / KB2) / a.n_cus : 0;
-  const int k_main = rounds >= 2 ? (int)(rounds * a.n_cus / pairs * KB2) : 0;
-  if (k_main > 0) {
-    const hipError_t e = launch_kv<D, 4, 2>(a, 0, k_main, stream);
+  if (a.k_main > 0) {
+    const hipError_t e = launch_kv<D, 4, 2>(a, 0, a.k_main, 1, stream);
     if (e != hipSuccess) return e;
   }
-  if (k_main < a.S) return launch_kv<D, 4, 4>(a, k_main, a.S, stream);
-  return hipSuccess;
+  if (a.k_main >= a.S) return hipSuccess;
+  const hipError_t e = launch_kv<D, 4, 4>(a, a.k_main, a.S, a.tail_parts, stream);
+  if (e != hipSuccess || a.tail_parts == 1) return e;
+  const int64_t per_item = (int64_t)(a.S - a.k_main) * a.Hkv * D;
+  const int64_t n = (int64_t)a.B * per_item;
+  hipLaunchKernelGGL(kv_part_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.part_dk,
+                     a.part_dv, a.tail_parts, n, per_item, (int64_t)a.S * a.Hkv * D, (int64_t)a.k_main * a.Hkv * D,
+                     a.dk, static_cast<__bf16*>(a.dv));
+  return hipGetLastError();
 }
 
 template <int D, int G>
@@ -697,6 +732,21 @@ hipError_t launch_q(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 int bwd_block_k(int group) { return 32 * (8 / group); }
+
+KvPlan kv_plan(int B, int S, int Hkv, int G, int n_cus) {
+  KvPlan p;
+  if (G != 4 || n_cus <= 0 || S <= 0) return p;
+  constexpr int KB2 = 128, KB4 = 64;
+  const int64_t pairs = (int64_t)B * Hkv;
+  // two-head blocks only where they fill at least two whole rounds of the CUs
+  const int64_t rounds = pairs * (S / KB2) / n_cus;
+  if (rounds < 2) return p;
+  p.k_main = (int)(rounds * n_cus / pairs * KB2);
+  // the rest: its steps split so that its blocks (one round or less) spread over the CUs
+  const int64_t tail_blocks = pairs * ((S - p.k_main + KB4 - 1) / KB4);
+  if (tail_blocks > 0) p.tail_parts = (int)std::max<int64_t>(1, std::min<int64_t>(4, n_cus / tail_blocks));
+  return p;
+}
 
 hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int B, int S, int Hq, int D,
                             hipStream_t stream) {
@@ -714,8 +764,8 @@ hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   if (a.D == 128)
-    return G == 1 ? launch_kv<128, 1, 1>(a, 0, a.S, stream) : G == 2 ? launch_kv<128, 2, 2>(a, 0, a.S, stream) : launch_kv_g4<128>(a, stream);
-  return G == 1 ? launch_kv<64, 1, 1>(a, 0, a.S, stream) : G == 2 ? launch_kv<64, 2, 2>(a, 0, a.S, stream) : launch_kv_g4<64>(a, stream);
+    return G == 1 ? launch_kv<128, 1, 1>(a, 0, a.S, 1, stream) : G == 2 ? launch_kv<128, 2, 2>(a, 0, a.S, 1, stream) : launch_kv_g4<128>(a, stream);
+  return G == 1 ? launch_kv<64, 1, 1>(a, 0, a.S, 1, stream) : G == 2 ? launch_kv<64, 2, 2>(a, 0, a.S, 1, stream) : launch_kv_g4<64>(a, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {

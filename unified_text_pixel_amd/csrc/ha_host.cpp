@@ -570,7 +570,8 @@ bool has_norm(const ha_prologue_desc* p) { return p && p->q_norm_weight; }
 
 struct BwdWorkspace {
   size_t row_limit, ranges, q_rot, k_rot, delta, dq_rot, dk_rot, dwq, dwk, dw_scratch, key_vis, tiles, tile_count,
-      total;
+      part_dk, part_dv, total;
+  ha::KvPlan kv;  // the dK/dV launch plan (G = 4)
 };
 
 BwdWorkspace bwd_workspace_layout(const ha_attn_desc* d, bool norm) {
@@ -596,6 +597,12 @@ BwdWorkspace bwd_workspace_layout(const ha_attn_desc* d, bool norm) {
     take(w.dw_scratch, (size_t)ha::dw_scratch_floats((int)D) * 4);
   }
   if (has_gen(d)) take_hole(d, nq, nk, &at, &w.key_vis, &w.tiles, &w.tile_count);
+  w.kv = ha::kv_plan(d->batch, d->seq_len, d->n_kv_heads, d->n_q_heads / d->n_kv_heads, plan_cus(d));
+  if (w.kv.tail_parts > 1) {  // the tail's partial dK and dV, fp32
+    const size_t part = (size_t)w.kv.tail_parts * B * (S - w.kv.k_main) * Hkv * D * 4;
+    take(w.part_dk, part);
+    take(w.part_dv, part);
+  }
   w.total = at;
   return w;
 }
@@ -1036,7 +1043,10 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   a.tile_count = hole.tile_count;
   a.kv_stride = ha::key_vis_stride(S);
   a.nk = nk;
-  a.n_cus = plan_cus(desc);
+  a.k_main = w.kv.k_main;
+  a.tail_parts = w.kv.tail_parts;
+  a.part_dk = w.kv.tail_parts > 1 ? reinterpret_cast<float*>(ws + w.part_dk) : nullptr;
+  a.part_dv = w.kv.tail_parts > 1 ? reinterpret_cast<float*>(ws + w.part_dv) : nullptr;
   if ((st = check_launch(ha::launch_bwd_dkdv(a, s), s, "backward dK dV")) != HA_OK) return st;
   if ((st = check_launch(ha::launch_bwd_dq(a, s), s, "backward dQ")) != HA_OK) return st;
   // through the rotary embedding and RMSNorm to the inputs

@@ -183,10 +183,21 @@ struct BwdArgs {
   const int32_t* tiles;
   const int32_t* tile_count;
   int32_t kv_stride, nk;
-  int32_t n_cus;             // CUs the dK/dV launches are shaped for (0: unknown)
-  // the dK/dV kernel's key range [k_begin, k_end) of one launch (set by launch_bwd_dkdv)
-  int32_t k_begin, k_end;
+  // dK/dV launch plan (G = 4, from the host's kv_plan): keys [0, k_main) two heads per step
+  // over 128-key blocks; keys [k_main, S) four heads per step over 64-key blocks, their
+  // 32-row steps cut into tail_parts ranges whose fp32 partial dK and dV go to
+  // part_dk / part_dv [tail_parts][B][S - k_main][Hkv][D] and are summed in part order
+  int32_t k_main, tail_parts;
+  float* part_dk;
+  float* part_dv;
+  // one launch's key range [k_begin, k_end) and step ranges (set by launch_bwd_dkdv)
+  int32_t k_begin, k_end, n_parts;
 };
+// dK/dV plan for G = 4 (zeros otherwise): see BwdArgs
+struct KvPlan {
+  int k_main = 0, tail_parts = 1;
+};
+KvPlan kv_plan(int B, int S, int Hkv, int G, int n_cus);
 hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int B, int S, int Hq, int D,
                             hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
