@@ -700,16 +700,16 @@ __global__ __launch_bounds__(256) void kv_part_sum_kernel(const float* part_dk, 
   dv[at] = static_cast<__bf16>(sv);
 }
 
-// G = 4 (see BwdArgs): the two-heads-per-step launch for keys [0, k_main), then the rest in
-// 64-key blocks, their steps in tail_parts ranges when few blocks are left
-template <int D>
-hipError_t launch_kv_g4(const BwdArgs& a, hipStream_t stream) {
+// keys [0, k_main) two heads per step over 128-key blocks (G = 4), the rest with HPS = G,
+// their steps in tail_parts ranges whose partial sums are then added (see BwdArgs)
+template <int D, int G>
+hipError_t launch_kv_plan(const BwdArgs& a, hipStream_t stream) {
   if (a.k_main > 0) {
     const hipError_t e = launch_kv<D, 4, 2>(a, 0, a.k_main, 1, stream);
     if (e != hipSuccess) return e;
   }
   if (a.k_main >= a.S) return hipSuccess;
-  const hipError_t e = launch_kv<D, 4, 4>(a, a.k_main, a.S, a.tail_parts, stream);
+  const hipError_t e = launch_kv<D, G, G>(a, a.k_main, a.S, a.tail_parts, stream);
   if (e != hipSuccess || a.tail_parts == 1) return e;
   const int64_t per_item = (int64_t)(a.S - a.k_main) * a.Hkv * D;
   const int64_t n = (int64_t)a.B * per_item;
@@ -735,16 +735,27 @@ int bwd_block_k(int group) { return 32 * (8 / group); }
 
 KvPlan kv_plan(int B, int S, int Hkv, int G, int n_cus) {
   KvPlan p;
-  if (G != 4 || n_cus <= 0 || S <= 0) return p;
-  constexpr int KB2 = 128, KB4 = 64;
+  if (n_cus <= 0 || S <= 0) return p;
   const int64_t pairs = (int64_t)B * Hkv;
-  // two-head blocks only where they fill at least two whole rounds of the CUs
-  const int64_t rounds = pairs * (S / KB2) / n_cus;
-  if (rounds < 2) return p;
-  p.k_main = (int)(rounds * n_cus / pairs * KB2);
-  // the rest: its steps split so that its blocks (one round or less) spread over the CUs
-  const int64_t tail_blocks = pairs * ((S - p.k_main + KB4 - 1) / KB4);
-  if (tail_blocks > 0) p.tail_parts = (int)std::max<int64_t>(1, std::min<int64_t>(4, n_cus / tail_blocks));
+  if (G == 4) {  // two-head blocks only where they fill at least two whole rounds of the CUs
+    const int64_t rounds = pairs * (S / CfgKV<128, 4, 2>::KB) / n_cus;
+    if (rounds >= 2) p.k_main = (int)(rounds * n_cus / pairs * CfgKV<128, 4, 2>::KB);
+  }
+  // the rest after two-head blocks, in blocks of 256/G keys: cut their steps into P ranges
+  // when that spreads the blocks over fewer rounds per unit of work (by 15% or more). Without
+  // a two-head part the blocks are many and the partial sums' traffic costs more than the
+  // rounds save (hd1024 in two ranges: 0.371 -> 0.387 ms).
+  if (p.k_main == 0) return p;
+  const int kb = 32 * (8 / G);
+  const int64_t blocks = pairs * ((S - p.k_main + kb - 1) / kb);
+  if (blocks <= 0) return p;
+  auto cost = [&](int parts) { return (double)((blocks * parts + n_cus - 1) / n_cus) / parts; };
+  double best = cost(1);
+  for (int parts = 2; parts <= 4; ++parts)
+    if (cost(parts) <= 0.85 * best) {
+      best = cost(parts);
+      p.tail_parts = parts;
+    }
   return p;
 }
 
@@ -764,8 +775,8 @@ hipError_t launch_bwd_delta(const void* out, const void* dout, float* delta, int
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   if (a.D == 128)
-    return G == 1 ? launch_kv<128, 1, 1>(a, 0, a.S, 1, stream) : G == 2 ? launch_kv<128, 2, 2>(a, 0, a.S, 1, stream) : launch_kv_g4<128>(a, stream);
-  return G == 1 ? launch_kv<64, 1, 1>(a, 0, a.S, 1, stream) : G == 2 ? launch_kv<64, 2, 2>(a, 0, a.S, 1, stream) : launch_kv_g4<64>(a, stream);
+    return G == 1 ? launch_kv_plan<128, 1>(a, stream) : G == 2 ? launch_kv_plan<128, 2>(a, stream) : launch_kv_plan<128, 4>(a, stream);
+  return G == 1 ? launch_kv_plan<64, 1>(a, stream) : G == 2 ? launch_kv_plan<64, 2>(a, stream) : launch_kv_plan<64, 4>(a, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {

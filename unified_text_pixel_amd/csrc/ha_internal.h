@@ -183,9 +183,9 @@ struct BwdArgs {
   const int32_t* tiles;
   const int32_t* tile_count;
   int32_t kv_stride, nk;
-  // dK/dV launch plan (G = 4, from the host's kv_plan): keys [0, k_main) two heads per step
-  // over 128-key blocks; keys [k_main, S) four heads per step over 64-key blocks, their
-  // 32-row steps cut into tail_parts ranges whose fp32 partial dK and dV go to
+  // dK/dV launch plan (the host's kv_plan): keys [0, k_main) two heads per step over
+  // 128-key blocks (G = 4 only); keys [k_main, S) G heads per step over 256/G-key blocks,
+  // their 32-row steps cut into tail_parts ranges whose fp32 partial dK and dV go to
   // part_dk / part_dv [tail_parts][B][S - k_main][Hkv][D] and are summed in part order
   int32_t k_main, tail_parts;
   float* part_dk;
@@ -193,7 +193,7 @@ struct BwdArgs {
   // one launch's key range [k_begin, k_end) and step ranges (set by launch_bwd_dkdv)
   int32_t k_begin, k_end, n_parts;
 };
-// dK/dV plan for G = 4 (zeros otherwise): see BwdArgs
+// dK/dV launch plan: see BwdArgs
 struct KvPlan {
   int k_main = 0, tail_parts = 1;
 };
