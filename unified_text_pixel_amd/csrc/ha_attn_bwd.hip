@@ -536,7 +536,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
   const int ic = row_ok ? i : 0;
   const int lim = row_ok ? a.row_limit[(int64_t)b * S + i] : 0;
   const int32_t* cnt = HOLE ? a.tile_count : a.ranges;
-  const int kfull = HOLE ? cnt[((int64_t)b * nq + qb) * 2 + 0] : 0;
+  const int kfull = cnt[((int64_t)b * nq + qb) * 2 + 0];
   const int kend = cnt[((int64_t)b * nq + qb) * 2 + 1];
   const int32_t* tlist = HOLE ? a.tiles + ((int64_t)b * nq + qb) * a.nk : nullptr;
   auto tile_at = [&](int t) __attribute__((always_inline)) {
@@ -583,6 +583,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
       kvd.issue(vbase, kvstride, tile_at(t + 1) * BK, S - 1, vn, wave);
     }
     const int tile = tile_at(t);
+    // a tile needs the per-pair mask unless every row of the block sees all of its keys and
+    // they lie inside the sequence
+    const bool masked = !(t < kfull && (tile + 1) * BK <= S);
     // LDS addresses from an opaque copy of the lane id, rebuilt each step (kept live
     // across the loop they would not fit in registers)
     int lo = lane;
@@ -596,49 +599,85 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x16 st = f32x16{}, pt = f32x16{};
-      const char* kr = kc + (32 * kt + lnx) * (2 * D);
-      const char* vr = vc + (32 * kt + lnx) * (2 * D);
+      // chunk 2kk + hi of K / V row 32kt + ln sits at (2kk) ^ kxx: the lane's kk = 0 offset
+      // XOR 32 kk (the row offset lies above the chunk bits)
+      int xr = (32 * kt + lnx) * (2 * D) + kxx * 16;
+      __asm__ volatile("" : "+v"(xr));
+      auto rd = [&](const char* buf, int kk) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(buf + (xr ^ (32 * kk)));
+      };
+      // operands of k-step kk + 1 are read while the two MFMAs of k-step kk run
+      bf16x8 fk[2], fv[2];
+      fk[0] = rd(kc, 0);
+      fv[0] = rd(vc, 0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const int off = ((2 * kk) ^ kxx) * 16;
-        st = mfma(*reinterpret_cast<const bf16x8*>(kr + off), qf[kk], st);
-        pt = mfma(*reinterpret_cast<const bf16x8*>(vr + off), of[kk], pt);
+        const int cur = kk & 1, nxt = cur ^ 1;
+        if (kk + 1 < D / 16) {
+          fk[nxt] = rd(kc, kk + 1);
+          fv[nxt] = rd(vc, kk + 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two DS reads of kk + 1
+        }
+        st = mfma(fk[cur], qf[kk], st);
+        pt = mfma(fv[cur], of[kk], pt);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then the two MFMAs of kk
       }
-      // Gen Images: the visibility of the lane's keys (runs of 4; key_vis rows are padded)
-      i32x4 vis[4];
+      f32x16 pe;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) vis[q4] = i32x4{S, S, S, S};
-      if (HOLE && t >= kfull) {
-        const int* kvp = a.key_vis + (int64_t)b * a.kv_stride + tile * BK + 32 * kt + 4 * hix;
+      for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(st[r] - l2);
+      if (masked) {
+        // element r is key tile BK + 32kt + 8(r/4) + 4hi + r%4: allowed below the row's
+        // limit and, with Gen Images, when its visibility ends after the row
+        const int rem = lim - (tile * BK + 32 * kt + 4 * hix);
+        i32x4 vis[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) vis[q4] = *reinterpret_cast<const i32x4*>(kvp + 8 * q4);
+        for (int q4 = 0; q4 < 4; ++q4) vis[q4] = i32x4{S, S, S, S};
+        if (HOLE) {
+          const int* kvp = a.key_vis + (int64_t)b * a.kv_stride + tile * BK + 32 * kt + 4 * hix;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) vis[q4] = *reinterpret_cast<const i32x4*>(kvp + 8 * q4);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = 8 * (r >> 2) + (r & 3) < rem && (!HOLE || i < vis[r >> 2][r & 3]);
+          pe[r] = ok ? pe[r] : 0.f;
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = tile * BK + 32 * kt + 8 * (r >> 2) + 4 * hix + (r & 3);
-        const bool ok = key < lim && (!HOLE || i < vis[r >> 2][r & 3]);
-        const float p = ok ? __builtin_amdgcn_exp2f(st[r] - l2) : 0.f;
-        zf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pt[r] - de));
-      }
+      for (int r = 0; r < 16; ++r) zf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(pe[r] * (pt[r] - de));
     }
     // dQ^T += K^T dZ^T: A = K^T (dims 32mt .., keys of step KS) gathered from LDS; lane t
     // of 16-lane group G16 points at key 16KS + 8rr + 4(G16 >> 1) + t/4, dims 32mt +
-    // 16(G16 & 1) + 4(t & 3)
+    // 16(G16 & 1) + 4(t & 3). Keys 16KS + r share swz(r) and 4mt + vcl = 4mt ^ vcl, so the
+    // address is the lane's (KS = 0, mt = 0) offset XOR 64 mt, plus KS * 16 rows.
     const int g16 = lo >> 4, t16 = lo & 15;
     const int vrow = 4 * (g16 >> 1) + (t16 >> 2);
     const int vclow = 2 * (g16 & 1) + ((t16 & 3) >> 1);
     const int vhalf = 8 * (t16 & 1);
+    int tl = vrow * (2 * D) + ((vclow ^ swz<C::CPR>(vrow)) * 16) + vhalf;
+    int tu = (vrow + 8) * (2 * D) + ((vclow ^ swz<C::CPR>(vrow + 8)) * 16) + vhalf;
+    __asm__ volatile("" : "+v"(tl), "+v"(tu));
+    auto trd = [&](int j) __attribute__((always_inline)) {
+      const int KS = j / (D / 32), mt = j % (D / 32);
+      const char* base = kc + KS * 16 * (2 * D);
+      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + (tl ^ (64 * mt))));
+      const bf16x4 up4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + (tu ^ (64 * mt))));
+      return __builtin_shufflevector(lo4, up4, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // the two transposing reads of (KS, mt) + 1 are issued while the MFMA of (KS, mt) runs
+    constexpr int NJ = (BK / 16) * (D / 32);
+    bf16x8 ka[2];
+    ka[0] = trd(0);
 #pragma unroll
-    for (int KS = 0; KS < BK / 16; ++KS) {
-      const int rl = 16 * KS + vrow, ru = rl + 8;
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const char* pl = kc + rl * (2 * D) + (((4 * mt + vclow) ^ swz<C::CPR>(rl)) * 16) + vhalf;
-        const char* pu = kc + ru * (2 * D) + (((4 * mt + vclow) ^ swz<C::CPR>(ru)) * 16) + vhalf;
-        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pl);
-        const bf16x4 up4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pu);
-        dq[mt] = mfma(__builtin_shufflevector(lo4, up4, 0, 1, 2, 3, 4, 5, 6, 7), zf[KS], dq[mt]);
+    for (int j = 0; j < NJ; ++j) {
+      const int cur = j & 1, nxt = cur ^ 1;
+      if (j + 1 < NJ) {
+        ka[nxt] = trd(j + 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of j + 1
       }
+      const int KS = j / (D / 32), mt = j % (D / 32);
+      dq[mt] = mfma(ka[cur], zf[KS], dq[mt]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // then the MFMA of j
     }
   };
   using P0 = std::integral_constant<int, 0>;
