@@ -141,9 +141,10 @@ template <int D, bool F32>
 __global__ __launch_bounds__(1024) void prologue_bwd_kernel(PrologueBwdArgs a) {
   constexpr int HALF = D / 2;
   constexpr int TPR = D / 16;
-  constexpr int MAXROWS = 1024 / TPR;  // head rows one workgroup can hold
   __shared__ float2 cs[HALF];
-  __shared__ float contrib[MAXROWS][D];  // this token's dy * x * r per head row
+  // this token's dy * x * r per head row, [Hq + Hkv][D] (sized at launch, none without
+  // RMSNorm: a small footprint keeps many tokens' loads in flight per CU)
+  extern __shared__ float contrib[];
   const int64_t token = blockIdx.x;
 
   if (a.rotate) {
@@ -192,8 +193,10 @@ __global__ __launch_bounds__(1024) void prologue_bwd_kernel(PrologueBwdArgs a) {
       const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
       const float k3 = r * r * r * xu / (float)D;
       for (int e = 0; e < 8; ++e) {
-        contrib[row][8 * c + e] = g1[e] * x1[e] * r;
-        contrib[row][HALF + 8 * c + e] = g2[e] * x2[e] * r;
+        if (a.dwq_part) {
+          contrib[row * D + 8 * c + e] = g1[e] * x1[e] * r;
+          contrib[row * D + HALF + 8 * c + e] = g2[e] * x2[e] * r;
+        }
         g1[e] = r * g1[e] * w[8 * c + e] - x1[e] * k3;
         g2[e] = r * g2[e] * w[HALF + 8 * c + e] - x2[e] * k3;
       }
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(1024) void prologue_bwd_kernel(PrologueBwdArgs a) {
       const int d = t % D;
       const bool q = t < D;
       float s = 0.f;
-      for (int r = q ? 0 : a.Hq, e = q ? a.Hq : a.Hq + a.Hkv; r < e; ++r) s += contrib[r][d];
+      for (int r = q ? 0 : a.Hq, e = q ? a.Hq : a.Hq + a.Hkv; r < e; ++r) s += contrib[r * D + d];
       (q ? a.dwq_part : a.dwk_part)[token * D + d] = s;
     }
   }
@@ -238,7 +241,8 @@ __global__ __launch_bounds__(1024) void dw_sum_kernel(const float* part, int64_t
 template <int D, bool F32>
 hipError_t launch_bwd(const PrologueBwdArgs& a, hipStream_t stream) {
   const int threads = ((a.Hq + a.Hkv) * (D / 16) + 63) / 64 * 64;
-  hipLaunchKernelGGL((prologue_bwd_kernel<D, F32>), dim3((unsigned)((int64_t)a.B * a.S)), dim3(threads), 0,
+  const size_t lds = a.dwq_part ? (size_t)(a.Hq + a.Hkv) * D * sizeof(float) : 0;
+  hipLaunchKernelGGL((prologue_bwd_kernel<D, F32>), dim3((unsigned)((int64_t)a.B * a.S)), dim3(threads), lds,
                      stream, a);
   return hipGetLastError();
 }
