@@ -570,8 +570,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
 
-  auto step = [&](auto par_tag, int t) __attribute__((always_inline)) {
+  auto step = [&](auto par_tag, auto mask_tag, int t) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool MASKED = decltype(mask_tag)::value;
     const char* const kc = PAR ? k1 : k0;
     const char* const vc = PAR ? v1 : v0;
     char* const kn = PAR ? k0 : k1;
@@ -583,9 +584,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
       kvd.issue(vbase, kvstride, tile_at(t + 1) * BK, S - 1, vn, wave);
     }
     const int tile = tile_at(t);
-    // a tile needs the per-pair mask unless every row of the block sees all of its keys and
-    // they lie inside the sequence
-    const bool masked = !(t < kfull && (tile + 1) * BK <= S);
     // LDS addresses from an opaque copy of the lane id, rebuilt each step (kept live
     // across the loop they would not fit in registers)
     int lo = lane;
@@ -625,7 +623,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
       f32x16 pe;
 #pragma unroll
       for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(st[r] - l2);
-      if (masked) {
+      if constexpr (MASKED) {
         // element r is key tile BK + 32kt + 8(r/4) + 4hi + r%4: allowed below the row's
         // limit and, with Gen Images, when its visibility ends after the row
         const int rem = lim - (tile * BK + 32 * kt + 4 * hix);
@@ -682,12 +680,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dq(BwdArgs a) {
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  using Full = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  // the walk's first tiles need no per-pair mask: every row of the block sees all of their
+  // keys and they lie inside the sequence (the list's inside FULL tiles, or tiles below
+  // kfull that end by S); an even count of them takes the unmasked step
+  const int nf = min(HOLE ? kfull : min(kfull, S / BK), kend) & ~1;
   int t = 0;
-  for (; t + 1 < kend; t += 2) {
-    step(P0{}, t);
-    step(P1{}, t + 1);
+  for (; t < nf; t += 2) {
+    step(P0{}, Full{}, t);
+    step(P1{}, Full{}, t + 1);
   }
-  if (t < kend) step(P0{}, t);
+  for (; t + 1 < kend; t += 2) {
+    step(P0{}, Masked{}, t);
+    step(P1{}, Masked{}, t + 1);
+  }
+  if (t < kend) step(P0{}, Masked{}, t);
 
   // dQ for the rotated q: scale * sum dZ k; element (mt, r) is dim 32mt + 8(r/4) + 4hi + r%4
   if (row_ok) {
