@@ -986,8 +986,8 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   if (empty(desc)) {
     // no tokens: the weight gradients are empty sums
     if (norm) {
-      if ((st = check_launch(ha::launch_dw_reduce(nullptr, 0, D, nullptr, dw_q, s), s, "dw")) != HA_OK) return st;
-      if ((st = check_launch(ha::launch_dw_reduce(nullptr, 0, D, nullptr, dw_k, s), s, "dw")) != HA_OK) return st;
+      if ((st = check_launch(ha::launch_dw_reduce(nullptr, nullptr, 0, D, nullptr, dw_q, dw_k, s), s, "dw")) != HA_OK)
+        return st;
     }
     return ok();
   }
@@ -1080,11 +1080,8 @@ ha_status ha_attn_bwd(const ha_attn_desc* desc, const ha_prologue_desc* pro, con
   if ((st = check_launch(ha::launch_prologue_bwd(p, s), s, "backward prologue")) != HA_OK) return st;
   if (norm) {
     float* scratch = reinterpret_cast<float*>(ws + w.dw_scratch);
-    if ((st = check_launch(ha::launch_dw_reduce(p.dwq_part, (int64_t)B * S, D, scratch, dw_q, s), s, "dw_q")) !=
-        HA_OK)
-      return st;
-    if ((st = check_launch(ha::launch_dw_reduce(p.dwk_part, (int64_t)B * S, D, scratch, dw_k, s), s, "dw_k")) !=
-        HA_OK)
+    if ((st = check_launch(ha::launch_dw_reduce(p.dwq_part, p.dwk_part, (int64_t)B * S, D, scratch, dw_q, dw_k, s), s,
+                           "dw")) != HA_OK)
       return st;
   }
   return ok();

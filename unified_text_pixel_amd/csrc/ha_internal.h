@@ -225,9 +225,11 @@ struct PrologueBwdArgs {
   uint8_t axis[64];
 };
 hipError_t launch_prologue_bwd(const PrologueBwdArgs& a, hipStream_t stream);
-// dw[d] = sum over rows of part[row][d] (fp32), for rows in [0, n), in a fixed order;
-// scratch holds dw_scratch_floats(D) floats of per-workgroup sums (unused when n == 0)
+// dw_q[d] = sum over rows of part_q[row][d] (fp32), for rows in [0, n), in a fixed order,
+// and dw_k from part_k alike; scratch holds dw_scratch_floats(D) floats of per-workgroup
+// sums (unused when n == 0)
 int dw_scratch_floats(int D);
-hipError_t launch_dw_reduce(const float* part, int64_t n, int D, float* scratch, float* dw, hipStream_t stream);
+hipError_t launch_dw_reduce(const float* part_q, const float* part_k, int64_t n, int D, float* scratch, float* dw_q,
+                            float* dw_k, hipStream_t stream);
 
 }  // namespace ha

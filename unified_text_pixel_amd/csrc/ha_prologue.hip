@@ -220,11 +220,15 @@ __global__ __launch_bounds__(1024) void prologue_bwd_kernel(PrologueBwdArgs a) {
 
 // dw[d] = sum over n rows of part[row][d], in two passes of fixed order: kDwBlocks
 // workgroups each sum a contiguous chunk of rows into out[block][d], then one workgroup
-// sums those. 1024 threads: 1024 / D threads per column, strided over the chunk.
+// sums those. 1024 threads: 1024 / D threads per column, strided over the chunk. The q and
+// k weights go together (blockIdx.y selects the pair of arrays).
 constexpr int kDwBlocks = 256;
 
-__global__ __launch_bounds__(1024) void dw_sum_kernel(const float* part, int64_t n, int D, float* out) {
+__global__ __launch_bounds__(1024) void dw_sum_kernel(const float* part_q, const float* part_k, int64_t n, int D,
+                                                      float* out_q, float* out_k) {
   __shared__ float acc[1024];
+  const float* part = blockIdx.y ? part_k : part_q;
+  float* out = blockIdx.y ? out_k : out_q;
   const int d = threadIdx.x % D, per = blockDim.x / D, j = threadIdx.x / D;
   const int64_t chunk = (n + gridDim.x - 1) / gridDim.x;
   const int64_t r0 = (int64_t)blockIdx.x * chunk, r1 = min(n, r0 + chunk);
@@ -254,16 +258,19 @@ hipError_t launch_prologue_bwd(const PrologueBwdArgs& a, hipStream_t stream) {
   return a.f32 ? launch_bwd<64, true>(a, stream) : launch_bwd<64, false>(a, stream);
 }
 
-int dw_scratch_floats(int D) { return kDwBlocks * D; }
+int dw_scratch_floats(int D) { return 2 * kDwBlocks * D; }
 
-hipError_t launch_dw_reduce(const float* part, int64_t n, int D, float* scratch, float* dw, hipStream_t stream) {
-  if (n == 0) {  // empty sum: one pass over no rows writes the zeros
-    hipLaunchKernelGGL(dw_sum_kernel, dim3(1), dim3(1024), 0, stream, part, n, D, dw);
+hipError_t launch_dw_reduce(const float* part_q, const float* part_k, int64_t n, int D, float* scratch, float* dw_q,
+                            float* dw_k, hipStream_t stream) {
+  if (n == 0) {  // empty sums: one pass over no rows writes the zeros
+    hipLaunchKernelGGL(dw_sum_kernel, dim3(1, 2), dim3(1024), 0, stream, part_q, part_k, n, D, dw_q, dw_k);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(dw_sum_kernel, dim3(kDwBlocks), dim3(1024), 0, stream, part, n, D, scratch);
-  hipLaunchKernelGGL(dw_sum_kernel, dim3(1), dim3(1024), 0, stream, (const float*)scratch, (int64_t)kDwBlocks, D,
-                     dw);
+  float* sq = scratch;
+  float* sk = scratch + (int64_t)kDwBlocks * D;
+  hipLaunchKernelGGL(dw_sum_kernel, dim3(kDwBlocks, 2), dim3(1024), 0, stream, part_q, part_k, n, D, sq, sk);
+  hipLaunchKernelGGL(dw_sum_kernel, dim3(1, 2), dim3(1024), 0, stream, (const float*)sq, (const float*)sk,
+                     (int64_t)kDwBlocks, D, dw_q, dw_k);
   return hipGetLastError();
 }
 
