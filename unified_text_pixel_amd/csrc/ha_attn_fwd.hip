@@ -320,12 +320,15 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // C operand of the first MFMA: zero, or -m on the careful pass)
   auto qk = [&](const char* kbuf, const f32x16& c0) {
     std::array<f32x16, 2> s;
-    const char* r0 = kbuf + krow * (2 * D);
+    // the lane's row offset and chunk swizzle, opaque: each k-step's address is rebuilt
+    // with one XOR instead of D/16 offsets held live across the loop
+    int kro = krow * (2 * D), kx16 = kx * 16;
+    __asm__ volatile("" : "+v"(kro), "+v"(kx16));
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int off = ((2 * kk) ^ kx) * 16;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(r0 + off);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(r0 + 32 * 2 * D + off);
+      const int off = kro + ((32 * kk) ^ kx16);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kbuf + off);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kbuf + off + 32 * 2 * D);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], kk == 0 ? c0 : s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], kk == 0 ? c0 : s[1], 0, 0, 0);
     }
@@ -379,16 +382,31 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
   // O^T += V^T P^T for one tile; the A operand of K step KS, dims 32mt.. comes from two
   // transposing reads (keys +0..3 and +8..11 of the lane's half)
   auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) {
+    // per dims block mt the lane's offset, opaque (the buffer + one register + a constant
+    // per K step), rebuilt per call rather than held live across the loop
+    int vo[D / 32];
 #pragma unroll
-    for (int KS = 0; KS < BK / 16; ++KS)
+    for (int mt = 0; mt < D / 32; ++mt) {
+      vo[mt] = vrow * (2 * D) + (((4 * mt) ^ vx) * 16) + vhalf;
+      __asm__ volatile("" : "+v"(vo[mt]));
+    }
+    auto rdv = [&](int j) __attribute__((always_inline)) {
+      const int KS = j / (D / 32), mt = j % (D / 32);
+      const char* p0 = vb + vo[mt] + 16 * KS * (2 * D);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+      const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * 2 * D));
+      return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // the A operand of product j + 1 is read while product j runs
+    constexpr int NJ = (BK / 16) * (D / 32);
+    bf16x8 vf[2];
+    vf[0] = rdv(0);
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const char* p0 = vb + (16 * KS + vrow) * (2 * D) + (((4 * mt) ^ vx) * 16) + vhalf;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * 2 * D));
-        const bf16x8 vf = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[KS], o[mt], 0, 0, 0);
-      }
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 1 < NJ) vf[(j + 1) & 1] = rdv(j + 1);
+      const int KS = j / (D / 32), mt = j % (D / 32);
+      o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j & 1], pf[KS], o[mt], 0, 0, 0);
+    }
   };
 
   // One main-pass step for tile t: land K_{t+1} and V_{t-1}, start the DMA of K_{t+2}
