@@ -209,6 +209,20 @@ def test_full_size_sampled_rows(name):
     assert np.array_equal(got[:, 0], np.repeat(v0, w.n_q_heads // w.n_kv_heads, axis=1))
 
 
+@pytest.mark.parametrize("name,group", [("hd2048", 3), ("edit", 6), ("hunyuan", 1), ("hunyuan_multigen", 5)])
+def test_full_size_kv_group_whole(name, group):
+    """Every row of every batch item for the G query heads of one KV head, at the full size
+    of the workload and in the launch configuration ha_attn_fwd chooses (the split plan on
+    the HunyuanImage layout, tile lists with Gen Images)."""
+    w = W.get_config(name)
+    x = W.generate(w)
+    out, _ = run_fwd(x)
+    G = w.n_q_heads // w.n_kv_heads
+    heads = list(range(group * G, (group + 1) * G))
+    want = oracle.hot_path(x, heads=heads)[:, :, heads]
+    compare(f64(out)[:, :, heads], want, w.dtype, f"{name} KV group {group}, whole ({w.seq_len} rows x {G} heads)")
+
+
 def test_hd1024_whole_output():
     """The 1024^2 HiDream-style workload (batch 2, 1282 tokens, 32 heads) compared with the
     oracle on every output element, in the launch configuration ha_attn_fwd chooses."""
