@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import (compare, desc_for, f64, prologue_for, refresh_bits, require_gpu,
+from gpu_helpers import (compare, desc_for, f64, plan, prologue_for, refresh_bits, require_gpu,
                          run_fwd, sample_rows, unsplit)
 from unified_text_pixel_amd import api, binding as B
 from workloads.device import to_device
@@ -221,6 +221,42 @@ def test_full_size_kv_group_whole(name, group):
     heads = list(range(group * G, (group + 1) * G))
     want = oracle.hot_path(x, heads=heads)[:, :, heads]
     compare(f64(out)[:, :, heads], want, w.dtype, f"{name} KV group {group}, whole ({w.seq_len} rows x {G} heads)")
+
+
+SLICE_CASES = {
+    "page1024": W.page_shape_configs()["page1024"],
+    "hd_small": SMALL["hd_small"],
+    "edit_small": SMALL["edit_small"],
+    "gca_small": SMALL["gca_small"],
+    "d64_bf16": SMALL["d64_bf16"],
+    "causal_rows_in_long_block": SMALL["causal_rows_in_long_block"],
+}
+
+
+@pytest.mark.parametrize("name", list(SLICE_CASES))
+def test_slice_workgroups_match_whole_blocks(name):
+    """With fewer work items than CUs (GQA group 4, plain tile ranges) every 32-row slice of a
+    query block runs as a workgroup of its own. Each row computes exactly as in a workgroup
+    that covers the whole block, so the two launches (the second planned for one CU, where
+    the items are not fewer than the CUs) agree bit for bit, output and row lse, and both
+    match the oracle."""
+    w = SLICE_CASES[name]
+    x = W.generate(w)
+    dev = to_device(x)
+    pro = prologue_for(w, dev)
+    res = []
+    for cus in (0, 1):
+        with plan(split_parts=1, plan_cus=cus):
+            desc = desc_for(w, x.segments)
+        ws = torch.empty(max(256, B.ha_attn_workspace_bytes(desc, pro)), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(dev["q"])
+        lse = torch.empty((w.batch, w.n_q_heads, w.seq_len), dtype=torch.float32, device="cuda")
+        B.ha_attn_fwd_lse(desc, pro, dev["q"], dev["k"], dev["v"], out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((out, lse))
+    assert torch.equal(res[0][0], res[1][0]), "output differs between slice and whole-block workgroups"
+    assert torch.equal(res[0][1], res[1][1]), "row lse differs between slice and whole-block workgroups"
+    compare(f64(res[0][0]), oracle.hot_path(x), w.dtype, f"{name} in slice workgroups")
 
 
 def test_hd1024_whole_output():

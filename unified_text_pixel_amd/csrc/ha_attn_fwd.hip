@@ -10,7 +10,9 @@
 //
 // Work item: one (batch, KV head, query block). Its eight waves (two per SIMD) cover the G
 // query heads that share the KV head, 32 query rows per wave, 256 / G rows per block, so
-// every K/V tile staged in LDS serves all of them. Per 64-key tile each wave computes
+// every K/V tile staged in LDS serves all of them. (With fewer work items than CUs and
+// G = 4, each 32-row slice of a block is a workgroup of its own, G waves, so that the
+// items spread over twice as many CUs; the rows compute exactly as before.) Per 64-key tile each wave computes
 //   S^T (keys x rows)  = K Q^T   with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q)
 //   O^T (dims x rows) += V^T P^T with the same instruction    (A = V^T from LDS, B = P)
 // In this orientation one lane holds one query row (lane % 32) and 16 of every 32 keys
@@ -104,9 +106,8 @@ __device__ inline float exp_tile(const f32x16 (&s)[2], float c, bf16x8 (&pf)[4])
 struct Item {
   int b, g, qb;
 };
-__device__ inline Item work_item(const AttnArgs& a) {
+__device__ inline Item work_item(const AttnArgs& a, int item) {
   const int nbg = a.B * a.Hkv;
-  const int item = blockIdx.x;
   int bg, slot;
   if (nbg % 8 == 0) {
     const int xcd = item % 8, s = item / 8;
@@ -138,10 +139,14 @@ struct Tile {
   __device__ static inline int vswz(int row) { return (0xCA60 >> (4 * (row & 3))) & (CPR - 1); }
 };
 
-template <int D, int G>
+// WS: one workgroup per 32-row slice of a query block (G waves), so that a problem with
+// fewer work items than CUs spreads over more of them; otherwise one workgroup covers the
+// whole block (G * TSUB waves).
+template <int D, int G, bool WS = false>
 struct CfgB {
-  static constexpr int TSUB = tsub_for(G);
-  static constexpr int NW = G * TSUB;
+  static constexpr int TSUB = tsub_for(G);    // 32-row slices per query block
+  static constexpr int WSUB = WS ? 1 : TSUB;  // slices per workgroup
+  static constexpr int NW = G * WSUB;
   static constexpr int NT = NW * 64;
   static constexpr int BQ = 32 * TSUB;
   static constexpr int IPW = Tile<D>::NI / NW;  // DMA instructions per wave per tile and tensor
@@ -156,7 +161,7 @@ struct CfgB {
 // instruction constant; the global address is a uniform base plus a per-lane offset.
 // Rows past the sequence end (only in the last tile) read its last row instead: masked
 // keys get P = 0 and that row is finite.
-template <int D, int G>
+template <int D, int G, bool WS>
 struct Dma {
   using TL = Tile<D>;
   const char* kbase;  // key 0 of this batch item and KV head (uniform)
@@ -184,8 +189,8 @@ struct Dma {
   template <bool ISV, bool CLAMP>
   __device__ inline void tile(int key0, char* buf) const {
 #pragma unroll
-    for (int j = 0; j < CfgB<D, G>::IPW; ++j) {
-      const int ins = wave * CfgB<D, G>::IPW + j;
+    for (int j = 0; j < CfgB<D, G, WS>::IPW; ++j) {
+      const int ins = wave * CfgB<D, G, WS>::IPW + j;
       const char* src;
       if constexpr (!CLAMP) {
         const char* g = (ISV ? vbase : kbase) + (key0 + TL::RPI * ins) * row_bytes;
@@ -209,10 +214,11 @@ struct Dma {
 //   LM & 2  work items come from a table: a query block may be split into parts, each
 //           walking a share of the positions and writing unnormalised partial results that
 //           combine_kernel merges.
-template <int D, int G, bool PRE, bool LSE, int LM>
-__global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
+template <int D, int G, bool PRE, bool LSE, int LM, bool WS = false>
+__global__ __launch_bounds__((CfgB<D, G, WS>::NT), 2) void attn_bf16(AttnArgs a) {
   constexpr bool KVIS = (LM & 1) != 0, ITEMS = (LM & 2) != 0, LIST = KVIS;
-  using C = CfgB<D, G>;
+  static_assert(!WS || LM == 0, "slice workgroups walk plain tile ranges");
+  using C = CfgB<D, G, WS>;
   using TL = Tile<D>;
   // K and V double buffers as four distinct arrays: a read of one buffer then never waits
   // for DMA still landing in another (the compiler tracks LDS DMA per array)
@@ -233,15 +239,29 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
     part = itm[2] & 0xffff;
     nparts = itm[2] >> 16;
     slot = itm[3];
-  } else {
-    const Item it = work_item(a);
+  }
+  int wslice = 0;  // WS: this workgroup's 32-row slice of the block
+  if constexpr (!ITEMS) {
+    int item = blockIdx.x;
+    if constexpr (WS) {
+      // the slices of a work item go to one XCD (workgroups go round-robin to the 8 XCDs),
+      // one after the other in dispatch order
+      if ((a.B * a.Hkv) % 8 == 0) {
+        wslice = (item / 8) % C::TSUB;
+        item = (item / (8 * C::TSUB)) * 8 + item % 8;
+      } else {
+        wslice = item % C::TSUB;
+        item /= C::TSUB;
+      }
+    }
+    const Item it = work_item(a, item);
     b = it.b;
     g = it.g;
     qb = it.qb;
   }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wave % G, tsub = wave / G;
+  const int hg = wave % G, tsub = WS ? wslice : wave / G;
   const int h = g * G + hg;
   const int hi = lane >> 5;
   const int S = a.S;
@@ -284,7 +304,7 @@ __global__ __launch_bounds__((CfgB<D, G>::NT), 2) void attn_bf16(AttnArgs a) {
       return t;
   };
   const float c = a.scale_log2e;
-  Dma<D, G> dma;
+  Dma<D, G, WS> dma;
   dma.init(a.k, a.v, b, g, S, a.Hkv, wave, lane);
 
   // K-operand reads: row 32kt + (lane & 31), logical chunk 2kk + hi
@@ -650,7 +670,7 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
   __shared__ float ks_lds[BK * C::P];
   __shared__ float v_lds[BK * C::P];
 
-  const Item it = work_item(a);
+  const Item it = work_item(a, blockIdx.x);
   const int b = it.b, g = it.g, qb = it.qb;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hg = wave % G, tsub = wave / G;
@@ -748,6 +768,23 @@ __global__ __launch_bounds__((CfgF<D, G>::NT), 1) void attn_f32(AttnArgs a) {
 template <int D, int G, int LM>
 void launch_bf16(const AttnArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(CfgB<D, G>::NT);
+  if constexpr (LM == 0 && G == 4) {
+    if (a.slices > 1) {
+      using C = CfgB<D, G, true>;
+      const dim3 wgrid(grid.x * C::TSUB), wblock(C::NT);
+      if (a.lse) {
+        if (a.q_prescaled)
+          hipLaunchKernelGGL((attn_bf16<D, G, true, true, LM, true>), wgrid, wblock, 0, stream, a);
+        else
+          hipLaunchKernelGGL((attn_bf16<D, G, false, true, LM, true>), wgrid, wblock, 0, stream, a);
+      } else if (a.q_prescaled) {
+        hipLaunchKernelGGL((attn_bf16<D, G, true, false, LM, true>), wgrid, wblock, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((attn_bf16<D, G, false, false, LM, true>), wgrid, wblock, 0, stream, a);
+      }
+      return;
+    }
+  }
   if (a.lse) {
     if (a.q_prescaled)
       hipLaunchKernelGGL((attn_bf16<D, G, true, true, LM>), grid, block, 0, stream, a);
@@ -794,6 +831,11 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int attn_slices(int head_dim, int group, bool f32) {
+  (void)head_dim;
+  return (!f32 && group == 4) ? tsub_for(group) : 1;
+}
 
 int attn_block_q(int head_dim, int group, bool f32) {
   (void)head_dim;

@@ -286,6 +286,8 @@ ha_status check_positions_debug(const ha_attn_desc* d, const ha_prologue_desc* p
   return HA_OK;
 }
 
+int plan_cus(const ha_attn_desc* d);
+
 // split query blocks on the device (null items: one work item per query block)
 struct SplitRun {
   int32_t* items = nullptr;
@@ -331,6 +333,11 @@ ha_status run_attn(const ha_attn_desc* d, const void* q, const void* k, const vo
   a.part_o = split.part_o;
   a.part_l = split.part_l;
   a.part_m = split.part_m;
+  // fewer work items than CUs (plain tile ranges): one workgroup per 32-row slice
+  a.slices = 1;
+  if (!hole.key_vis && !split.items &&
+      (int64_t)d->batch * d->n_kv_heads * a.nq_run < plan_cus(d))
+    a.slices = ha::attn_slices(d->head_dim, d->n_q_heads / d->n_kv_heads, a.f32 != 0);
   return check_launch(ha::launch_attn(a, stream), stream, "attention");
 }
 

@@ -118,8 +118,13 @@ struct AttnArgs {
   float* part_o;
   float* part_l;
   float* part_m;
+  // workgroups per query block: 1, or (bf16, group 4, plain tile ranges) one per 32-row
+  // slice, which spreads a problem with fewer work items than CUs over more of them
+  int32_t slices;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+// Workgroups per query block when the work items are too few to fill the CUs (1: no slices).
+int attn_slices(int head_dim, int group, bool f32);
 
 // Merge of split query blocks: splits [n_splits][4] of (b * Hkv + g, query block, first
 // slot, parts); writes out (bf16) and, when lse is set, the row lse.
