@@ -274,3 +274,55 @@ def test_autograd_matches_direct_calls():
     assert torch.equal(out.detach(), out2)
     for got, want in zip((q.grad, k.grad, v.grad, wq.grad, wk.grad), ref):
         assert torch.equal(got, want)
+
+
+def test_backward_offsets_past_2_31_sampled():
+    """Training forward and backward with q, out, dO and dq past 2^31 elements (1100 batch
+    items x 2048 tokens x 8 query heads x 128; items from 1024 on lie wholly beyond element
+    2^31), RMSNorm and 1D rotary: the 64-bit offsets of every backward kernel. Inputs drawn
+    on the device from a seeded generator; the dq, dk, dv and lse of sampled items against
+    the oracle's gradients of those items (the norm-weight gradients sum over all 1100
+    items and are checked for finiteness only)."""
+    from unified_text_pixel_amd import api
+    nb, S, Hq, Hkv, D = 1100, 2048, 8, 2, 128
+    assert 1024 * S * Hq * D == 2 ** 31
+    seg = np.tile(np.array([[[0, 70, C], [70, S - 70, F]]], dtype=np.int32), (nb, 1, 1))
+    w = small([W.Segment(C, 70), W.Segment(F, S - 70)], batch=nb, hq=Hq, hkv=Hkv, d=D, rope="1d")
+    desc = desc_for(w, seg)
+    gen = torch.Generator(device="cuda").manual_seed(17)
+
+    def draw(h):
+        t = torch.empty((nb, S, h, D), dtype=torch.bfloat16, device="cuda")
+        for b0 in range(0, nb, 128):  # fp32 draws in slices, rounded to bf16
+            t[b0:b0 + 128] = torch.randn((min(128, nb - b0), S, h, D), generator=gen, device="cuda")
+        return t
+
+    q, k, v, dout = draw(Hq), draw(Hkv), draw(Hkv), draw(Hq)
+    wrng = np.random.default_rng(18)
+    w_q = (1 + 0.02 * wrng.standard_normal(D)).astype(np.float32)
+    w_k = (1 + 0.02 * wrng.standard_normal(D)).astype(np.float32)
+    pos = np.broadcast_to(np.arange(S, dtype=np.int32)[None, :, None], (nb, S, 1))
+    cs = api.rope_table(w.rope_theta, D, S)
+    pro = B.PrologueDesc("1d", torch.from_numpy(np.ascontiguousarray(pos)).cuda(), cs, cs.shape[0],
+                         torch.from_numpy(w_q).cuda(), torch.from_numpy(w_k).cuda(), w.norm_eps,
+                         w.mrope_sections)
+    ws = torch.empty(max(256, B.ha_attn_workspace_bytes(desc, pro), B.ha_attn_bwd_workspace_bytes(desc, pro)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((nb, Hq, S), dtype=torch.float32, device="cuda")
+    B.ha_attn_fwd_lse(desc, pro, q, k, v, out, lse, ws)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dwq = torch.full((D,), float("nan"), device="cuda")
+    dwk = torch.full((D,), float("nan"), device="cuda")
+    B.ha_attn_bwd(desc, pro, q, k, v, out, lse, dout, dq, dk, dv, dwq, dwk, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dwq).all() and torch.isfinite(dwk).all()
+    for b in (0, 1024, nb - 1):
+        x1 = W.Inputs(workload=w.replace(batch=1), q=f64(q[b:b + 1]), k=f64(k[b:b + 1]), v=f64(v[b:b + 1]),
+                      q_bits=None, k_bits=None, v_bits=None, w_q=w_q, w_k=w_k, positions=pos[b:b + 1],
+                      segments=seg[b:b + 1])
+        want = oracle.path_backward(x1, f64(dout[b:b + 1]))
+        for name in ("dq", "dk", "dv"):
+            got = f64({"dq": dq, "dk": dk, "dv": dv}[name][b:b + 1])
+            check(f"item {b} of {nb} {name}", got, want[name])
+        check_lse(f64(lse[b:b + 1]), oracle.path_lse(x1))

@@ -139,6 +139,88 @@ def test_classifier_many_batch_items():
     check_labels(w, seg)
 
 
+def test_classifier_max_sequence_sampled():
+    """The largest sequence the descriptor admits (HA_MAX_SEQ_LEN = 2^22 tokens), two batch
+    items with every prefix kind and cuts that are not tile multiples: the row limits of
+    sampled rows (segment edges, both ends, random rows) and the ranges of the query blocks
+    holding segment edges against the oracle's mask rows, ranges through the tile-label
+    definition (any / all over each tile of the block). The whole mask, 2^44 pairs, is out
+    of reach."""
+    S = 1 << 22  # HA_MAX_SEQ_LEN of include/ha_attn.h
+    seg = np.array([
+        [[0, 1000, C], [1000, 2_000_000, F], [2_001_000, 1_048_576, G], [3_049_576, 777, C],
+         [3_050_353, S - 3_050_353, G]],
+        [[0, 333, C], [333, 1_000_003, G], [1_000_336, 65_536, G], [1_065_872, 3_000_000, F],
+         [4_065_872, S - 4_065_872, C]],
+    ], dtype=np.int32)
+    w = small([W.Segment(C, S)], batch=2, hq=4, hkv=1)  # the descriptor's shape only
+    desc = desc_for(w, seg)
+    bq, bk, nq, nk = B.ha_tile_shape(desc)
+    ranges = torch.empty((2, nq, 2), dtype=torch.int32, device="cuda")
+    lim = torch.empty((2, S), dtype=torch.int32, device="cuda")
+    B.ha_classify_tiles(desc, None, ranges, lim)
+    torch.cuda.synchronize()
+    ranges, lim = ranges.cpu().numpy(), lim.cpu().numpy()
+    rng = np.random.default_rng(7)
+    q0 = S - nq * bq
+    for b in range(2):
+        edges = {e for s0, L, _ in seg[b] for e in (s0, s0 + 1, s0 + L - 1, s0 + L - 2)} | {0, S - 1}
+        rows = np.array(sorted({r for r in edges if 0 <= r < S} | set(rng.integers(0, S, 16).tolist())))
+        M = oracle.mask_rows(seg[b], S, rows)
+        n = M.sum(axis=1)
+        assert all(M[r, :n[r]].all() for r in range(len(rows))), "oracle rows are not prefixes"
+        assert np.array_equal(lim[b, rows], n), f"batch {b}: row limits differ"
+        for qb in sorted({(int(s0) - q0) // bq for s0, _, _ in seg[b]} | {nq - 1}):
+            r0, r1 = max(q0 + qb * bq, 0), q0 + (qb + 1) * bq
+            Mb = oracle.mask_rows(seg[b], S, np.arange(r0, r1)).reshape(r1 - r0, nk, bk)
+            full, none = Mb.all(axis=(0, 2)), ~Mb.any(axis=(0, 2))
+            want = (int(full.sum()), int(nk - none.sum()))
+            assert tuple(ranges[b, qb]) == want, f"batch {b} block {qb}: ranges {tuple(ranges[b, qb])} != {want}"
+
+
+def test_offsets_past_2_31_sampled():
+    """q and out past 2^31 elements (1100 batch items x 2048 tokens x 8 query heads x 128;
+    items from 1024 on lie wholly beyond element 2^31): the 64-bit offsets of the
+    classifier, the q/k prologue (RMSNorm, 1D rotary), the attention kernel and its stores.
+    Inputs drawn on the device from a seeded generator; sampled items, rows and every head
+    against the oracle's whole path on those items' tensors."""
+    nb, S, Hq, Hkv, D = 1100, 2048, 8, 2, 128
+    assert 1024 * S * Hq * D == 2 ** 31
+    seg = np.tile(np.array([[[0, 70, C], [70, S - 70, F]]], dtype=np.int32), (nb, 1, 1))
+    w = small([W.Segment(C, 70), W.Segment(F, S - 70)], batch=nb, hq=Hq, hkv=Hkv, d=D, rope="1d")
+    desc = desc_for(w, seg)
+    gen = torch.Generator(device="cuda").manual_seed(13)
+
+    def draw(h):
+        t = torch.empty((nb, S, h, D), dtype=torch.bfloat16, device="cuda")
+        for b0 in range(0, nb, 128):  # fp32 draws in slices, rounded to bf16
+            t[b0:b0 + 128] = torch.randn((min(128, nb - b0), S, h, D), generator=gen, device="cuda")
+        return t
+
+    q, k, v = draw(Hq), draw(Hkv), draw(Hkv)
+    wrng = np.random.default_rng(14)
+    w_q = (1 + 0.02 * wrng.standard_normal(D)).astype(np.float32)
+    w_k = (1 + 0.02 * wrng.standard_normal(D)).astype(np.float32)
+    pos = np.broadcast_to(np.arange(S, dtype=np.int32)[None, :, None], (nb, S, 1))
+    dev_pos = torch.from_numpy(np.ascontiguousarray(pos)).cuda()
+    cs = api.rope_table(w.rope_theta, D, S)
+    pro = B.PrologueDesc("1d", dev_pos, cs, cs.shape[0], torch.from_numpy(w_q).cuda(),
+                         torch.from_numpy(w_k).cuda(), w.norm_eps, w.mrope_sections)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, B.ha_attn_workspace_bytes(desc, pro)), dtype=torch.uint8, device="cuda")
+    B.ha_attn_fwd(desc, pro, q, k, v, out, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.array(sorted({0, 1, 69, 70, 71, 1000, S - 1} | set(rng.integers(0, S, 8).tolist())))
+    heads = list(range(Hq))
+    for b in (0, 1023, 1024, nb - 1):
+        x1 = W.Inputs(workload=w.replace(batch=1), q=f64(q[b:b + 1]), k=f64(k[b:b + 1]), v=f64(v[b:b + 1]),
+                      q_bits=None, k_bits=None, v_bits=None, w_q=w_q, w_k=w_k, positions=pos[b:b + 1],
+                      segments=seg[b:b + 1])
+        want = oracle.hot_path_rows(x1, 0, rows, heads)
+        compare(f64(out[b, rows]), want, "bf16", f"item {b} of {nb} ({len(rows)} rows x {Hq} heads)")
+
+
 # ---------------------------------------------------------------- prologue
 @pytest.mark.parametrize("name", ["hd_small", "gca_small", "d64_bf16", "f32_mixed", "f32_d128"])
 def test_prologue_parity(name):
