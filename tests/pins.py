@@ -575,6 +575,26 @@ def pin_rows_match_whole_path():
                 assert np.abs(got - want).max() <= 1e-12, (b, rows.tolist(), heads.tolist())
 
 
+def pin_heads_match_whole_path():
+    """hot_path restricted to some query heads (the checker of the full-size GPU tests that
+    compare one KV group's heads whole) equals the whole call's entries for those heads, and
+    leaves every other head unset."""
+    rng = np.random.default_rng(37)
+    for w in _rows_layouts():
+        x = W.generate(w)
+        whole = oracle.pipeline.hot_path(x)
+        grp = w.n_q_heads // w.n_kv_heads
+        for g in range(w.n_kv_heads):
+            heads = list(range(g * grp, (g + 1) * grp))
+            if rng.random() < 0.5:  # and an arbitrary subset
+                heads = sorted(rng.choice(w.n_q_heads, size=int(rng.integers(1, w.n_q_heads + 1)),
+                                          replace=False).tolist())
+            part = oracle.pipeline.hot_path(x, heads=heads)
+            assert np.abs(part[:, :, heads] - whole[:, :, heads]).max() <= 1e-12, (w.name, heads)
+            others = [h for h in range(w.n_q_heads) if h not in heads]
+            assert np.isnan(part[:, :, others]).all(), (w.name, heads)
+
+
 def pin_backward_groups_match_whole():
     """path_backward restricted to some KV groups (the checker of the full-size backward
     GPU tests) equals the entries of the whole call, pinned by finite differences and torch

@@ -317,6 +317,33 @@ MUTATIONS.update({
 })
 
 
+_orig_attention = oracle.masked_attention.attention
+
+
+def _attention_heads_enumerated(q, k, v, masks, scale=None, dtype=np.float64, heads=None, row_chunk=1024):
+    """heads= mistake: the i-th requested query head reads the KV head of its place in the
+    list (i // group) instead of its own (h // group)."""
+    if heads is None:
+        return _orig_attention(q, k, v, masks, scale=scale, dtype=dtype, row_chunk=row_chunk)
+    heads = list(heads)
+    group = q.shape[2] // k.shape[2]
+    out = np.full(q.shape, np.nan, dtype=dtype)
+    for i, h in enumerate(heads):
+        kk, vv = np.array(k, copy=True), np.array(v, copy=True)
+        src = min(i // group, k.shape[2] - 1)
+        kk[:, :, h // group] = k[:, :, src]
+        vv[:, :, h // group] = v[:, :, src]
+        out[:, :, h] = _orig_attention(q, kk, vv, masks, scale=scale, dtype=dtype, heads=[h],
+                                       row_chunk=row_chunk)[:, :, h]
+    return out
+
+
+MUTATIONS.update({
+    "heads_subset_enumerated_kv": ([(oracle.pipeline, "attention", _attention_heads_enumerated)],
+                                   ["pin_heads_match_whole_path"]),
+})
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     patches, pin_names = MUTATIONS[name]
