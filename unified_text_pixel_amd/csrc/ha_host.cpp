@@ -15,7 +15,6 @@
 #include <cstdlib>
 #include <cstring>
 #include <functional>
-#include <queue>
 #include <string>
 #include <vector>
 
@@ -409,16 +408,15 @@ std::vector<int> block_costs(const ha_attn_desc* d, int b, int bq, int nq, int n
 }
 
 // makespan of list scheduling in the given order on n machines
-double list_schedule(const std::vector<double>& costs, int n) {
-  std::priority_queue<double, std::vector<double>, std::greater<double>> q;
-  for (int i = 0; i < n; ++i) q.push(0.0);
+// (loads: the machines' loads, a min-heap reused between calls)
+double list_schedule(const std::vector<double>& costs, int n, std::vector<double>& loads) {
+  loads.assign(n, 0.0);  // all equal: already a heap
   double ms = 0.0;
   for (double c : costs) {
-    double t = q.top();
-    q.pop();
-    t += c;
-    ms = std::max(ms, t);
-    q.push(t);
+    std::pop_heap(loads.begin(), loads.end(), std::greater<double>());
+    loads.back() += c;
+    ms = std::max(ms, loads.back());
+    std::push_heap(loads.begin(), loads.end(), std::greater<double>());
   }
   return ms;
 }
@@ -439,20 +437,22 @@ SplitPlan plan_split(const ha_attn_desc* d) {
   if ((int64_t)(nbg / groups) * nq > ha::kPlanMaxItems) return plan;  // the device sort's limit
   const int cus = std::max(1, affine ? n_cus / 8 : n_cus);
   constexpr double kItem = 4.0;  // fixed cost of a work item (start, last tile, stores), in tiles
-  std::vector<int> cost;  // of batch item cost_b
-  int cost_b = -1;
+  // This runs on the host at every call, so its buffers are reused: the block costs of each
+  // batch item (made on first use), a group's costs, the two sorted runs of a candidate
+  // list, the list and the machine loads of the simulation.
+  std::vector<std::vector<int>> costs(d->batch);
+  std::vector<int> it, prev_it;
+  std::vector<double> whole_c, part_c, c, loads;
+  int prev_best = 1;
   int slot = 0, n_splits = 0, longest = 0;
   for (int x = 0; x < groups; ++x) {
-    std::vector<int> it;  // costs in the group's item order: pairs x, x + 8, ..., blocks from the last
+    it.clear();  // costs in the group's item order: pairs x, x + 8, ..., blocks from the last
     for (int bg = affine ? x : 0; bg < nbg; bg += affine ? 8 : 1) {
       const int b = bg / d->n_kv_heads;
-      if (b != cost_b) {
-        cost = block_costs(d, b, bq, nq, nk);
-        cost_b = b;
-      }
-      for (int qb = nq - 1; qb >= 0; --qb) it.push_back(cost[qb]);
+      if (costs[b].empty()) costs[b] = block_costs(d, b, bq, nq, nk);
+      for (int qb = nq - 1; qb >= 0; --qb) it.push_back(costs[b][qb]);
     }
-    std::stable_sort(it.begin(), it.end(), std::greater<int>());
+    std::sort(it.begin(), it.end(), std::greater<int>());  // equal costs are interchangeable
     const int n = (int)it.size();
     int best = 1, k = 0, heavy = 0;
     if (n > 0) {
@@ -463,18 +463,29 @@ SplitPlan plan_split(const ha_attn_desc* d) {
         k = 0;
         heavy = n;
         best = force;
-      } else {
+      } else if (x > 0 && it == prev_it) {
+        best = prev_best;  // the same sorted costs as the previous group: the same decision
+      } else if (k < heavy) {  // else no heavy item is left to split
         double best_ms = 0.0, whole_ms = 0.0;
         for (int parts : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
-          if (parts > 1 && (k == heavy || parts > cmax)) break;
-          std::vector<double> c;
+          if (parts > 1 && parts > cmax) break;
+          // the candidate list in descending cost: the whole items (it is sorted, so they
+          // are) merged with the parts of the split ones (sorted too); the makespan of list
+          // scheduling does not depend on the order among equal costs
+          whole_c.clear();
+          part_c.clear();
           for (int i = 0; i < n; ++i) {
-            const bool split = parts > 1 && i >= k && i < heavy;
-            for (int p = 0; p < (split ? parts : 1); ++p)
-              c.push_back((split ? std::ceil((double)it[i] / parts) : (double)it[i]) + kItem);
+            if (parts > 1 && i >= k && i < heavy) {
+              const double pc = std::ceil((double)it[i] / parts) + kItem;
+              for (int p = 0; p < parts; ++p) part_c.push_back(pc);
+            } else {
+              whole_c.push_back((double)it[i] + kItem);
+            }
           }
-          std::stable_sort(c.begin(), c.end(), std::greater<double>());
-          const double ms = list_schedule(c, cus) + (parts > 1 ? kItem : 0.0);  // + the merge
+          c.resize(whole_c.size() + part_c.size());
+          std::merge(whole_c.begin(), whole_c.end(), part_c.begin(), part_c.end(), c.begin(),
+                     std::greater<double>());
+          const double ms = list_schedule(c, cus, loads) + (parts > 1 ? kItem : 0.0);  // + the merge
           if (parts == 1) whole_ms = ms;
           if (parts == 1 || ms < best_ms) {
             best = parts;
@@ -483,6 +494,8 @@ SplitPlan plan_split(const ha_attn_desc* d) {
         }
         if (best_ms > 0.97 * whole_ms) best = 1;  // not worth a merge
       }
+      prev_it.swap(it);  // it is rebuilt for the next group
+      prev_best = best;
     }
     plan.n[x] = n;
     plan.best[x] = best;
