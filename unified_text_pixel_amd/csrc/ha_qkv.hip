@@ -321,21 +321,22 @@ __global__ __launch_bounds__((CfgP<WN, WM, MT, BK, NST>::NT), 1) void qkv_kernel
 
 // The kernel's configurations: 2 heads x 256 tokens per workgroup (8 waves of 128 features x
 // 64 tokens), and for the tail 1 head x 128 tokens (4 waves of 128 x 32, a quarter of a main
-// tile, so the tail's tiles spread over about as many CUs as a round has); K in stages of
-// 32 in a ring of 5 (160 KB of LDS for the main tile, 80 KB for the tail's: three stages in
-// flight behind the one computed).
+// tile, so the tail's tiles spread over about as many CUs as a round has); K in a ring of 5
+// stages (three in flight behind the one computed), 32 wide for the main tile and 64 for the
+// tail's (160 KB of LDS each; the wider stage gives the tail's four waves twice the products
+// between two barriers).
 constexpr int kWN = 2, kWM = 4, kBK = 32, kNST = 5;
-constexpr int kTailWN = 1, kTailWM = 4, kTailMT = 1;
+constexpr int kTailWN = 1, kTailWM = 4, kTailMT = 1, kTailBK = 64;
 using Main = CfgP<kWN, kWM, 2, kBK, kNST>;
 
-template <int WN, int WM, int MT>
+template <int WN, int WM, int MT, int BK = kBK>
 hipError_t launch_part(const QkvArgs& a, hipStream_t stream) {
-  using C = CfgP<WN, WM, MT, kBK, kNST>;
+  using C = CfgP<WN, WM, MT, BK, kNST>;
   const int nM = (a.T - a.m_begin + C::BM - 1) / C::BM;
   const int nN = (a.Hq + 2 * a.Hkv + WN - 1) / WN;
   const int total = nM * nN;
   const int grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((qkv_kernel<WN, WM, MT, kBK, kNST>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((qkv_kernel<WN, WM, MT, BK, kNST>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -361,7 +362,7 @@ hipError_t launch_qkv(const QkvArgs& a, int n_cus, hipStream_t stream) {
   if (m_main * Main::BM < a.T) {
     p = a;
     p.m_begin = m_main * Main::BM;
-    return launch_part<kTailWN, kTailWM, kTailMT>(p, stream);
+    return launch_part<kTailWN, kTailWM, kTailMT, kTailBK>(p, stream);
   }
   return hipSuccess;
 }
