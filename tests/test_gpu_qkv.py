@@ -96,24 +96,31 @@ def test_plain_projection_without_prologue():
         check(f"plain {n}", f64(got), want)
 
 
-def test_full_size_sampled_tokens():
-    """The hd2048 layer: 2 x 4354 tokens, hidden 4096, GQA 32/8 (6144 outputs per token), in
-    the benchmark's launch configuration; sampled tokens of both batch items against the oracle."""
-    w = W.get_config("hd2048")
+@pytest.mark.parametrize("name", ["hd2048", "hunyuan"])
+def test_full_size_sampled_tokens(name):
+    """A full layer, hidden 4096, GQA 32/8 (6144 outputs per token), in the benchmark's launch
+    configuration: the hd2048 layer (2 x 4354 tokens, RMSNorm + mRoPE) and the HunyuanImage
+    layer (6016 tokens, 2D rotary on images and 1D on text, no norm; a different split between
+    the main tiles and the tail); sampled tokens of every batch item (both ends, the edges of
+    the main and tail tiles, random ones) against the oracle."""
+    w = W.get_config(name)
     x_in = W.generate(w)
     proj = W.generate_projection(w, 4096)
     q, k, v, desc, _ = run_qkv(w, x_in, proj, prescale=True)
     scale = float(np.float32(B.ha_q_prescale(desc)))
     rng = np.random.default_rng(3)
+    S = w.seq_len
     for b in range(w.batch):
-        rows = np.unique(np.r_[0, 1, 255, 256, 257, 4353, rng.integers(0, w.seq_len, 40)])
+        rows = np.unique(np.r_[0, 1, 255, 256, 257, 5375, 5376, 5377, S - 1,
+                               rng.integers(0, S, 40)])
+        rows = rows[rows < S]
         sub = dataclasses.replace(x_in, workload=w.replace(batch=1), q=x_in.q[b:b + 1, rows],
                                   k=x_in.k[b:b + 1, rows], v=x_in.v[b:b + 1, rows],
                                   positions=x_in.positions[b:b + 1, rows], segments=x_in.segments[b:b + 1])
         q_ref, k_ref, v_ref = oracle.qkv_prologue(sub, proj.x[b:b + 1, rows], proj.w_qkv)
-        check(f"hd2048 item {b} q", f64(q[b, rows]), q_ref[0] * scale)
-        check(f"hd2048 item {b} k", f64(k[b, rows]), k_ref[0])
-        check(f"hd2048 item {b} v", f64(v[b, rows]), v_ref[0])
+        check(f"{name} item {b} q", f64(q[b, rows]), q_ref[0] * scale)
+        check(f"{name} item {b} k", f64(k[b, rows]), k_ref[0])
+        check(f"{name} item {b} v", f64(v[b, rows]), v_ref[0])
 
 
 def test_feeds_attention():
