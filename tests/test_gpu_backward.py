@@ -220,6 +220,24 @@ def test_backward_hd2048_one_group():
     check("hd2048 dv", got["dv"][1, :, 3], want["dv"][0, :, 3])
 
 
+def test_backward_edit_one_group():
+    """The editing layout at full size (text, a full 64x64 generation grid, a causal 64x64
+    reference grid; S = 8448), whose dK/dV plan differs from the 2048^2 one; the oracle
+    computes KV group 6 of batch item 0 (its 4 query heads' dq, its dk and dv)."""
+    w = W.get_config("edit")
+    print("case edit: group 6 of item 0", flush=True)
+    x = W.generate(w)
+    dout = output_grad(w, seed=82)
+    got = run_train(x, dout)
+    one = dataclasses.replace(x, workload=w.replace(batch=1), q=x.q[:1], k=x.k[:1], v=x.v[:1],
+                              positions=x.positions[:1], segments=x.segments[:1])
+    want = oracle.path_backward(one, dout[:1], groups=[6])
+    heads = slice(24, 28)
+    check("edit dq", got["dq"][0, :, heads], want["dq"][0, :, heads])
+    check("edit dk", got["dk"][0, :, 6], want["dk"][0, :, 6])
+    check("edit dv", got["dv"][0, :, 6], want["dv"][0, :, 6])
+
+
 def test_backward_multigen_one_group():
     """The multi-image training layout at full size (text, a 32x32 Gen Image, text, a
     64x64 Gen Image, text; S = 6016); the oracle computes KV group 5 (its 4 query heads'
