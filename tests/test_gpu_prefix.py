@@ -140,3 +140,19 @@ def test_api_forward_from_over_steps(rope, norm):
         assert torch.equal(got, want), f"step {step}"
     with pytest.raises(ValueError):
         attn.forward_from(q, k, v, 67)
+
+
+def test_prefix_step_full_size_hd2048():
+    """The 2048^2 layout at full size (2 x 4354 tokens, GQA 32/8): a step from the end of the
+    258-token text prefix equals the whole path bit for bit, and sampled rows after the prefix
+    match the oracle on the step-1 inputs."""
+    w = W.get_config("hd2048")
+    print("case hd2048 full size, p=258", flush=True)
+    out, whole, x = two_steps(w, 258)
+    assert torch.equal(out, whole), "prefix step differs from the whole path"
+    got = f64(out)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.r_[258, 259, 321, 322, 4353, rng.integers(258, w.seq_len, 20)])
+    for b in range(w.batch):
+        want = oracle.hot_path_rows(x, b, rows, list(range(w.n_q_heads)))
+        compare(got[b, rows], want, "bf16", f"hd2048 prefix step, item {b} ({len(rows)} rows x 32 heads)")
