@@ -66,3 +66,37 @@ def test_graph_replays_equal_eager(name, parts):
         ref = attn(q, k, v)
         torch.cuda.synchronize()
         assert torch.equal(out, ref), (name, parts, r, float((out.float() - ref.float()).abs().max()))
+
+
+@pytest.mark.parametrize("name,group", [("hunyuan", 1), ("page1024", 5)])
+def test_graph_full_size(name, group):
+    """Full-size layouts in a graph: the HunyuanImage interleave (S = 6016), whose call takes
+    the device-built split plan, partial results and merge on the device's CUs, and the
+    page-exact 1024^2 shape, whose attention runs in slice workgroups. Every replay equals the
+    eager call bit for bit; the first matches the oracle on one KV group's heads."""
+    cfg = dict(W.CONFIGS)
+    cfg.update(W.page_shape_configs())
+    w = cfg[name]
+    print(f"case {name} full size, KV group {group}", flush=True)
+    x = W.generate(w)
+    dev = to_device(x)
+    attn = attention_for(w, dev)
+    q, k, v = dev["q"].clone(), dev["k"].clone(), dev["v"].clone()
+    replay, out = attn.graphed(q, k, v)
+    torch.cuda.synchronize()
+    replay()
+    torch.cuda.synchronize()
+    G = w.n_q_heads // w.n_kv_heads
+    heads = list(range(group * G, (group + 1) * G))
+    compare(f64(out)[:, :, heads], oracle.hot_path(x, heads=heads)[:, :, heads], w.dtype,
+            f"{name} graph replay, KV group {group}")
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    for r in range(3):
+        for t in (q, k, v):
+            t.copy_(torch.randn(t.shape, generator=gen, device="cuda").to(t.dtype))
+        torch.cuda.synchronize()
+        replay()
+        torch.cuda.synchronize()
+        ref = attn(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), (name, r, float((out.float() - ref.float()).abs().max()))
