@@ -335,6 +335,18 @@ __global__ __launch_bounds__((CfgB<D, G, WS>::NT), 2) void attn_bf16(AttnArgs a)
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * hi);
+  // A training forward (row lse) of q without the scale takes q' = bf16(scale log2(e) q),
+  // rounded as the prologue rounds it: the backward rebuilds P from those same q' values and
+  // this lse, so both must score with the same q' (with the scale applied in fp32 here
+  // instead, a large component common to every key would shift each row's scores by the
+  // rounding of q' between the two passes, and P's rows would no longer sum to 1)
+  constexpr bool PS = PRE || LSE;  // scores in log2 units: q prescaled, given or made here
+  if constexpr (!PRE && LSE) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = static_cast<__bf16>(static_cast<float>(qf[ks][e]) * c);
+  }
 
   // S^T + c0 for the 64 keys of a K buffer, the two 32-key halves interleaved (c0 is the
   // C operand of the first MFMA: zero, or -m on the careful pass)
@@ -459,7 +471,7 @@ __global__ __launch_bounds__((CfgB<D, G, WS>::NT), 2) void attn_bf16(AttnArgs a)
     if (FAST || t >= 1) pv(vr, pfp);
     bool vis = true;
     if (!FAST) vis = mask(sc, t);
-    const float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pf));
+    const float ts = wave_pair_sum(exp_tile<PS>(sc, c, pf));
     if constexpr (TRACK) {
       // a row that has seen no key of its part yet has nothing to be out of range
       seen = seen || vis;
@@ -553,7 +565,7 @@ __global__ __launch_bounds__((CfgB<D, G, WS>::NT), 2) void attn_bf16(AttnArgs a)
       const auto s0 = qk(kb, negm);
       f32x16 sc[2] = {s0[0], s0[1]};
       mask(sc, u);
-      float ts = wave_pair_sum(exp_tile<PRE>(sc, c, pa));
+      float ts = wave_pair_sum(exp_tile<PS>(sc, c, pa));
       const bool bad = !(ts <= kHi) || !(l + ts >= kLo);
       if (__builtin_amdgcn_ballot_w64(bad)) {
         float mx = sc[0][0];
@@ -562,7 +574,7 @@ __global__ __launch_bounds__((CfgB<D, G, WS>::NT), 2) void attn_bf16(AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
         mx = wave_pair_max(mx);
-        if (!PRE) mx *= c;
+        if (!PS) mx *= c;
         float sh = fmaxf(mx, __builtin_amdgcn_logf(l));
         sh = (bad && sh > -INFINITY) ? sh : 0.f;
         mref += sh;
@@ -572,14 +584,14 @@ __global__ __launch_bounds__((CfgB<D, G, WS>::NT), 2) void attn_bf16(AttnArgs a)
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
         l *= alpha;
-        const float shs = PRE ? sh : sh / c;  // in accumulator units
+        const float shs = PS ? sh : sh / c;  // in accumulator units
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           negm[r] -= shs;
           sc[0][r] -= shs;
           sc[1][r] -= shs;
         }
-        ts = wave_pair_sum(exp_tile<PRE>(sc, c, pa));
+        ts = wave_pair_sum(exp_tile<PS>(sc, c, pa));
       }
       l += ts;
       pv(vb, pa);
