@@ -477,16 +477,19 @@ def clock_window(step, sets, stream, useful, seconds=1.0):
                 "attn_tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS})
     # the fraction at the measured clock, from the first reading that is plausible: a clock
     # under which the measured throughput would exceed the dense peak is not the clock the
-    # kernel ran at (some boards report a fixed low level through the clock-info query)
+    # kernel ran at, and neither is one that reads the same in every sample of a window of
+    # back-to-back launches, during which the firmware moves the core clock with power and
+    # temperature (some boards report a fixed level through these queries)
     for key in ("sclk_mhz", "xcd_sclk_mhz"):
         if out.get(key):
             peak = 256 * 4096 * out[key]["median"] * 1e6 / 1e12
-            if tf <= peak:
+            constant = out[key]["samples"] > 10 and out[key]["min"] == out[key]["max"]
+            if tf <= peak and not constant:
                 out["clock_used"] = key
                 out["bf16_peak_at_measured_sclk_tflops"] = peak
                 out["frac_at_measured_sclk"] = tf / peak
                 break
-            out.setdefault("implausible", []).append(key)
+            out.setdefault("implausible", []).append(key + (" (constant over the window)" if constant else " (above the dense peak)"))
     return out
 
 
