@@ -149,7 +149,10 @@ constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int x = blockIdx.x, tid = threadIdx.x;
   const int n = a.n[x], best = a.best[x], k = a.k[x], heavy = a.heavy[x];
-  __shared__ int cost[kPlanMaxItems], order[kPlanMaxItems], c1[kPlanMaxItems], mult[kPlanMaxItems];
+  __shared__ int cost[kPlanMaxItems], order[kPlanMaxItems];
+  // per sorted position: the cost of one entry of the final list and how many entries (parts)
+  // the item makes, side by side so that one read serves the count below
+  __shared__ int2 cm[kPlanMaxItems];
   auto pair_of = [&](int j) { return a.affine ? x + 8 * (j / a.nq) : j / a.nq; };
   for (int j = tid; j < n; j += kPlanThreads) {
     const int b = pair_of(j) / a.Hkv, qb = a.nq - 1 - j % a.nq;
@@ -166,19 +169,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int r = tid; r < n; r += kPlanThreads) {
     const bool split = best > 1 && r >= k && r < heavy;
     const int c = cost[order[r]];
-    c1[r] = split ? (c + best - 1) / best : c;
-    mult[r] = split ? best : 1;
+    cm[r] = make_int2(split ? (c + best - 1) / best : c, split ? best : 1);
   }
   __syncthreads();
   for (int r = tid; r < n; r += kPlanThreads) {
-    const int cr = c1[r];
+    const int2 mine = cm[r];
+    const int cr = mine.x, mult = mine.y;
     int f = 0;  // entries of the final list before this item's first part
-    for (int u = 0; u < n; ++u) f += (c1[u] > cr || (c1[u] == cr && u < r)) ? mult[u] : 0;
+    int u = 0;
+    for (; u + 8 <= n; u += 8) {  // eight reads in flight, then the eight counts
+      int2 e[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) e[t] = cm[u + t];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) f += (e[t].x > cr || (e[t].x == cr && u + t < r)) ? e[t].y : 0;
+    }
+    for (; u < n; ++u) {
+      const int2 e = cm[u];
+      f += (e.x > cr || (e.x == cr && u < r)) ? e.y : 0;
+    }
     const int j = order[r];
     const int bg = pair_of(j), qb = a.nq - 1 - j % a.nq;
-    const bool split = mult[r] > 1;
+    const bool split = mult > 1;
     const int slot0 = split ? a.slot_base[x] + (r - k) * best : -1;
-    for (int p = 0; p < mult[r]; ++p) {
+    for (int p = 0; p < mult; ++p) {
       if (f + p >= a.len[x]) break;  // cannot happen: the list holds exactly len entries
       int32_t* e = a.items + ((int64_t)(f + p) * a.groups + x) * 4;
       e[0] = bg;
