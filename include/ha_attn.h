@@ -264,7 +264,10 @@ ha_status ha_qkv_prologue(const ha_attn_desc* desc, const ha_prologue_desc* pro,
 
 /* ha_attn_fwd, also writing the row log-sum-exp the backward needs: lse, DEVICE fp32
  * [batch][n_q_heads][seq_len], the natural log of sum_j exp(scale q_i . k_j) over the keys
- * row i attends (q, k after the prologue). Same workspace as ha_attn_fwd. */
+ * row i attends (q, k after the prologue). The scores are those ha_attn_bwd rebuilds: with
+ * q' = scale log2(e) q rounded to bf16, which the prologue writes, or which this call
+ * forms from q itself when pro is NULL and q is not prescaled; so the lse and the
+ * backward's probabilities agree to fp32 rounding. Same workspace as ha_attn_fwd. */
 ha_status ha_attn_fwd_lse(const ha_attn_desc* desc, const ha_prologue_desc* pro, const void* q,
                           const void* k, const void* v, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream);
