@@ -51,3 +51,16 @@ def test_pairs_of_the_whole_batch(name):
     table = W.segment_table(w)
     pairs = sum(bench.allowed_pairs(table[b], w.seq_len) for b in range(w.batch))
     assert pairs == w.batch * gold["allowed_pairs_per_batch_item"]
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_is_refused(argv, env):
+    """One GPU only: more exits with status 2 and says so, before anything touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                       env={**os.environ, **env}, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
